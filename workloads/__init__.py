@@ -1,0 +1,237 @@
+"""Seeded synthetic inputs for the attention-forward workloads.
+
+This module only *draws* inputs: random bf16 tensors, sequence lengths and
+the packed-sequence offsets.  It contains none of the attention arithmetic,
+so both the CPU oracle (``oracle/``) and the HIP path's tests and benchmark
+may use it without sharing any of the method.
+
+bf16 tensors are returned as ``numpy.uint16`` arrays holding the raw bf16
+bit patterns (numpy has no bf16 type).  Values are drawn in float32 with
+``numpy.random.default_rng(seed)`` (PCG64) and rounded to bf16 with
+round-to-nearest-even.  Draw order per workload: sequence lengths (packed
+workload only), then Q, K, V, each with ``standard_normal(dtype=float32)``.
+
+Layouts: q, k are ``[T, H, d_qk]``, v is ``[T, H, d_v]`` (token-major, heads
+interleaved), where T is the total token count; ``cu_seqlens`` is int32
+``[B+1]`` with ``cu_seqlens[b]`` the first token of sequence b.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "workload",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "make_inputs",
+    "make_custom_inputs",
+    "ramp_strength",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention-forward workload (shapes and value distribution)."""
+
+    key: str
+    B: int                 # number of sequences
+    H: int                 # heads
+    N: int                 # (max) sequence length
+    d_qk: int
+    d_v: int
+    causal: bool
+    varlen: bool = False   # lengths drawn uniformly in [len_lo, len_hi]
+    len_lo: int = 0
+    len_hi: int = 0
+    ramp: bool = False     # per-key linear ramp on Q/K (logits grow along the sequence)
+    description: str = ""
+    scale: float = field(default=0.0)
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale else 1.0 / math.sqrt(self.d_qk)
+
+
+# The five workloads the forward pass is checked and timed on.
+WORKLOADS = {
+    "small_noncausal_b1h2n256d64": Workload(
+        "small_noncausal_b1h2n256d64", B=1, H=2, N=256, d_qk=64, d_v=64, causal=False,
+        description="non-causal, B=1 H=2 N=256 d=64, N(0,1), scale 1/8"),
+    "noncausal_b4h16n4096d128": Workload(
+        "noncausal_b4h16n4096d128", B=4, H=16, N=4096, d_qk=128, d_v=128, causal=False,
+        description="non-causal, B=4 H=16 N=4096 d=128, N(0,1), scale 1/sqrt(128)"),
+    "causal_b2h16n16384d128": Workload(
+        "causal_b2h16n16384d128", B=2, H=16, N=16384, d_qk=128, d_v=128, causal=True,
+        description="causal, B=2 H=16 N=16384 d=128, N(0,1), scale 1/sqrt(128)"),
+    "causal_b2h32n8192dqk192dv128": Workload(
+        "causal_b2h32n8192dqk192dv128", B=2, H=32, N=8192, d_qk=192, d_v=128, causal=True,
+        description="causal split head dims d_qk=192 d_v=128, B=2 H=32 N=8192, scale 1/sqrt(192)"),
+    "varlen_causal_16seq_h32d128_ramp": Workload(
+        "varlen_causal_16seq_h32d128_ramp", B=16, H=32, N=32768, d_qk=128, d_v=128, causal=True,
+        varlen=True, len_lo=512, len_hi=32768, ramp=True,
+        description="packed causal, 16 sequences with lengths U[512,32768], H=32 d=128, "
+                    "Q/K N(0,1) plus a per-key linear ramp (logit std ~4)"),
+}
+
+_ORDER = list(WORKLOADS)
+
+
+def workload(key_or_index) -> Workload:
+    """Look a workload up by key or by its 1-based position in ``WORKLOADS``."""
+    if isinstance(key_or_index, int):
+        return WORKLOADS[_ORDER[key_or_index - 1]]
+    return WORKLOADS[key_or_index]
+
+
+def f32_to_bf16_bits(x: np.ndarray, out: np.ndarray | None = None,
+                     scratch: np.ndarray | None = None) -> np.ndarray:
+    """Round float32 values to bf16 (round-to-nearest-even); return uint16 bit patterns.
+
+    ``out`` (uint16) and ``scratch`` (uint32, same size) may be passed to avoid
+    fresh allocations when converting in chunks.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = np.empty(u.shape, dtype=np.uint32) if scratch is None else scratch.reshape(u.shape)
+    np.right_shift(u, np.uint32(16), out=r)
+    np.bitwise_and(r, np.uint32(1), out=r)
+    np.add(r, np.uint32(0x7FFF), out=r)
+    np.add(r, u, out=r)
+    np.right_shift(r, np.uint32(16), out=r)
+    if out is None:
+        return r.astype(np.uint16)
+    out[...] = r.reshape(out.shape)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+class _Chunker:
+    """Reusable float32/uint32 chunk buffers for drawing and rounding."""
+
+    def __init__(self, elems: int):
+        self.f = np.empty(elems, dtype=np.float32)
+        self.s = np.empty(elems, dtype=np.uint32)
+
+    def fill(self, rng, out2d: np.ndarray, add_rows: np.ndarray | None = None):
+        """Fill uint16 [rows, cols] with bf16(N(0,1) + add_rows[row])."""
+        rows, cols = out2d.shape
+        per = max(1, self.f.size // max(cols, 1))
+        for t0 in range(0, rows, per):
+            t1 = min(rows, t0 + per)
+            n = (t1 - t0) * cols
+            z = self.f[:n].reshape(t1 - t0, cols)
+            rng.standard_normal(dtype=np.float32, out=z)
+            if add_rows is not None:
+                z += add_rows[t0:t1, None].astype(np.float32)
+            f32_to_bf16_bits(z, out=out2d[t0:t1], scratch=self.s[:n])
+
+
+_CHUNK_ELEMS = 1 << 22
+
+
+def _normal_bf16(rng: np.random.Generator, shape, chunker=None) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16, generated in chunks to bound memory."""
+    T = shape[0]
+    row = int(np.prod(shape[1:]))
+    out = np.empty((T, row), dtype=np.uint16)
+    (chunker or _Chunker(_CHUNK_ELEMS)).fill(rng, out)
+    return out.reshape(shape)
+
+
+def ramp_strength(d: int) -> float:
+    """Ramp coefficient beta = gamma for the packed workload.
+
+    With u = 1/sqrt(d) * ones(d), queries get +beta*u and key j of a sequence
+    of length L gets +gamma*t_j*u, t_j = j/(L-1).  The scaled logit of a causal
+    pair then has variance 1 + (beta^2 + gamma^2 E[t^2] + beta^2 gamma^2 Var t)/d
+    with E[t^2] = 1/6 and Var t = 1/18 over causal pairs; beta = gamma = 13.255
+    gives a logit standard deviation of about 4 at d = 128.
+    """
+    del d
+    return 13.255
+
+
+def _ramp_bf16(rng, L: int, H: int, d: int, coef_rows: np.ndarray, chunker=None):
+    """bf16(N(0,1) + coef_rows[t]) for every element of token t, shape [L, H, d]."""
+    out = np.empty((L, H * d), dtype=np.uint16)
+    (chunker or _Chunker(_CHUNK_ELEMS)).fill(rng, out, add_rows=coef_rows)
+    return out.reshape(L, H, d)
+
+
+def make_inputs(wl, seed: int = 0) -> dict:
+    """Draw the seeded inputs of a workload.
+
+    Returns a dict with keys q, k, v (uint16 bf16 bits), cu_seqlens (int32
+    [B+1]), lengths (int64 [B]), B, H, N (max length), d_qk, d_v, causal,
+    scale, T.
+    """
+    if not isinstance(wl, Workload):
+        wl = workload(wl)
+    rng = np.random.default_rng(seed)
+    if wl.varlen:
+        lengths = rng.integers(wl.len_lo, wl.len_hi, size=wl.B, endpoint=True).astype(np.int64)
+    else:
+        lengths = np.full(wl.B, wl.N, dtype=np.int64)
+    cu = np.zeros(wl.B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    H = wl.H
+    if wl.ramp:
+        beta = ramp_strength(wl.d_qk)
+        u = 1.0 / math.sqrt(wl.d_qk)
+        ch = _Chunker(_CHUNK_ELEMS)
+        qs, ks, vs = [], [], []
+        # Q for all sequences, then K, then V (the draw order of the module doc).
+        for b in range(wl.B):
+            L = int(lengths[b])
+            qs.append(_ramp_bf16(rng, L, H, wl.d_qk, np.full(L, beta * u), ch))
+        for b in range(wl.B):
+            L = int(lengths[b])
+            t = np.arange(L, dtype=np.float64) / max(L - 1, 1)
+            ks.append(_ramp_bf16(rng, L, H, wl.d_qk, beta * t * u, ch))
+        for b in range(wl.B):
+            L = int(lengths[b])
+            vs.append(_normal_bf16(rng, (L, H, wl.d_v), ch))
+        q = np.concatenate(qs, axis=0)
+        k = np.concatenate(ks, axis=0)
+        v = np.concatenate(vs, axis=0)
+    else:
+        ch = _Chunker(_CHUNK_ELEMS)
+        q = _normal_bf16(rng, (T, H, wl.d_qk), ch)
+        k = _normal_bf16(rng, (T, H, wl.d_qk), ch)
+        v = _normal_bf16(rng, (T, H, wl.d_v), ch)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu.astype(np.int32), lengths=lengths,
+                B=wl.B, H=H, N=int(lengths.max()) if wl.B else 0, d_qk=wl.d_qk, d_v=wl.d_v,
+                causal=wl.causal, scale=wl.softmax_scale(), T=T, key=wl.key)
+
+
+def make_custom_inputs(lengths, H: int, d_qk: int, d_v: int, seed: int = 0,
+                       std: float = 1.0, mean: float = 0.0) -> dict:
+    """Seeded N(mean, std^2) bf16 inputs for arbitrary (ragged) sequence lengths.
+
+    Used for edge cases: empty sequences, lengths that are not a multiple of
+    any tile size, single-token sequences.
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+
+    def draw(d):
+        x = rng.standard_normal((T, H, d), dtype=np.float32) * np.float32(std) + np.float32(mean)
+        return f32_to_bf16_bits(x)
+
+    q = draw(d_qk)
+    k = draw(d_qk)
+    v = draw(d_v)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu.astype(np.int32), lengths=lengths,
+                B=len(lengths), H=H, N=int(lengths.max()) if len(lengths) else 0,
+                d_qk=d_qk, d_v=d_v, T=T)
