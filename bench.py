@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
+                    [--tau 8.0] [--poly 0] [--no-cpu-baseline]
+
+A step is one call of attn_fwd over the whole workload (all query blocks of
+all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
+d=128 (bf16 inputs, fp32 accumulation).  Inputs are seeded synthetic bf16
+draws resident in HBM before timing starts.
+
+Printed (one JSON line on stdout):
+  value      whole-job TFLOP/s = algorithmic FLOP * K / wall time of the K steps
+             (bracketed by device synchronisations)
+  roofline   the kernel's per-launch average duration from HIP events recorded
+             on the launch stream over the timed region; achieved TFLOP/s
+             against the dense bf16 MFMA peak; HBM traffic per launch from
+             committed rocprofv3 counter summaries when they match the current
+             kernel source, else null
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload (whole (sequence, head) pairs until ~10 s have elapsed),
+             scaled to TFLOP/s with the same FLOP convention
+
+FLOP convention: 4*B*H*N^2*d (non-causal, d_qk = d_v = d), 2*B*H*N^2*(d_qk+d_v)
+in general, halved when causal; packed sequences sum the per-sequence counts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "noncausal_b4h16n4096d128"
+KERNEL_SOURCES = ["exact_attention_57_amd/csrc/attn_fwd_kernel.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(lengths, H, d_qk, d_v, causal) -> float:
+    tot = 0.0
+    for L in lengths:
+        f = 2.0 * H * float(L) * float(L) * (d_qk + d_v)
+        tot += f / 2 if causal else f
+    return tot
+
+
+def compulsory_bytes(T, H, d_qk, d_v) -> float:
+    """Read Q, K, V once, write O (bf16) and LSE (fp32) once."""
+    return T * H * (2 * d_qk * 2 + d_v * 2 + d_v * 2 + 4)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, variant: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.json, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("variant") != variant:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle on whole (sequence, head) pairs until the budget is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    cu = inp["cu_seqlens"]
+    H = inp["H"]
+    pairs = [(b, h) for b in range(len(cu) - 1) for h in range(H) if cu[b + 1] > cu[b]]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(pairs))
+    done_flops = 0.0
+    n = 0
+    t0 = time.perf_counter()
+    for idx in order:
+        b, h = pairs[idx]
+        s, e = int(cu[b]), int(cu[b + 1])
+        sub_cu = np.array([0, e - s])
+        oracle.attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
+                         sub_cu, inp["causal"], inp["scale"])
+        done_flops += algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {len(pairs)} (sequence, head) pairs, fp64 NumPy/BLAS, {dt:.1f} s",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold (log2); <0 = always")
+    ap.add_argument("--poly", type=int, default=0, help="sixteenths of exps on the software exp2")
+    ap.add_argument("--schedule", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU kernel only: the attention forward pass shards "
+              "over (sequence, head) pairs with no exchange, so run it with --gpus 1 "
+              f"(got --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_57_amd as ea
+    import workloads
+
+    wl = workloads.workload(args.workload)
+    log(f"bench: drawing inputs for {wl.key}")
+    inp = workloads.make_inputs(wl, seed=0)
+    T, H = inp["T"], inp["H"]
+    lengths = [int(x) for x in inp["lengths"]]
+    flops = algorithmic_flops(lengths, H, wl.d_qk, wl.d_v, wl.causal)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda() if wl.varlen else None
+    o = torch.empty((T, H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
+               scale=inp["scale"], rescale_threshold_log2=args.tau,
+               poly_exp_sixteenths=args.poly, schedule=args.schedule, stream=stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    variant = f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
+    traffic = load_traffic(wl.key, variant)
+    out = {
+        "metric": "attention fwd TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": wl.key, "B": wl.B, "H": H, "N": inp["N"], "T": T,
+                   "d_qk": wl.d_qk, "d_v": wl.d_v, "causal": wl.causal,
+                   "packed": wl.varlen, "variant": variant, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(ev_ms, 4),
+                     "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

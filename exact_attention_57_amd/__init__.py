@@ -1,0 +1,199 @@
+"""Python binding of libattn.so, the MI355X fused attention forward pass.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``.  Torch is used for
+device memory (``data_ptr``) and for the current HIP stream.
+
+The library must be built first (``python exact_attention_57_amd/build.py``);
+importing this package without it raises ImportError -- there is no fallback
+of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "lib", "fwd", "fwd_raw", "debug_exp2", "strerror", "version",
+    "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
+    "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
+    "SUPPORTED_DIMS", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_UNSUPPORTED = -3
+ATTN_ERR_ALIGN = -4
+ATTN_ERR_VALUE = -5
+ATTN_ERR_LAUNCH = -6
+SCHEDULE_LONGEST_FIRST = 0
+SCHEDULE_NATURAL = 1
+SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str = "attn_fwd"):
+        self.status = status
+        super().__init__(f"{where} failed with status {status}: {strerror(status)}")
+
+
+class FwdOpts(ctypes.Structure):
+    _fields_ = [
+        ("rescale_threshold_log2", ctypes.c_float),
+        ("poly_exp_sixteenths", ctypes.c_int),
+        ("schedule", ctypes.c_int),
+        ("stats", ctypes.c_void_p),
+    ]
+
+
+def _hip_runtimes_mapped():
+    """Distinct libamdhip64 files mapped into this process (Linux /proc/self/maps)."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    found.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return found
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python exact_attention_57_amd/build.py`")
+    # torch ships its own HIP runtime.  Load it first so that libattn.so's
+    # dependency on libamdhip64.so.7 resolves to that same, already-loaded
+    # copy: two HIP runtimes in one process cannot share streams or memory.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {sorted(runtimes)}")
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_fwd.argtypes = fwd_args
+    L.attn_fwd.restype = i32
+    L.attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(FwdOpts)]
+    L.attn_fwd_ex.restype = i32
+    L.attn_fwd_opts_default.argtypes = [ctypes.POINTER(FwdOpts)]
+    L.attn_fwd_opts_default.restype = None
+    L.attn_strerror.argtypes = [i32]
+    L.attn_strerror.restype = ctypes.c_char_p
+    L.attn_debug_exp2.argtypes = [vp, vp, i32, i32, vp]
+    L.attn_debug_exp2.restype = i32
+    L.attn_version.argtypes = []
+    L.attn_version.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.attn_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib.attn_version())
+
+
+def default_opts() -> FwdOpts:
+    o = FwdOpts()
+    lib.attn_fwd_opts_default(ctypes.byref(o))
+    return o
+
+
+def fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, B, H, N, d_qk, d_v, scale, causal,
+            stream, opts: FwdOpts | None = None) -> int:
+    """Call attn_fwd_ex with raw integer pointers; returns the status code."""
+    return int(lib.attn_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
+                               int(d_qk), int(d_v), float(scale), int(bool(causal)), stream,
+                               ctypes.byref(opts) if opts is not None else None))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
+        scale=None, rescale_threshold_log2=8.0, poly_exp_sixteenths=0,
+        schedule=SCHEDULE_LONGEST_FIRST, stats=None, stream=None):
+    """Fused attention forward on torch tensors.
+
+    Fixed length: q, k [B, N, H, d_qk], v [B, N, H, d_v] (or [T, H, d] with
+    ``cu_seqlens=None`` and ``max_seqlen`` = N, T = B*N).  Packed: q, k
+    [T, H, d_qk], v [T, H, d_v] with ``cu_seqlens`` (int32 device [B+1]) and
+    ``max_seqlen`` (>= longest sequence).  bf16, contiguous, on the GPU.
+
+    Returns (o, lse): o bf16 shaped like v, lse fp32 [H, T].  Outputs are
+    allocated with torch when not given.  ``stats``: optional uint64/int64
+    device tensor of 4 counters that the kernel adds to.
+    """
+    import torch
+    if q.dim() == 4:
+        B, N, H, d_qk = q.shape
+        if cu_seqlens is not None:
+            raise ValueError("4-D inputs are fixed length; pass [T, H, d] with cu_seqlens")
+        T = B * N
+    elif q.dim() == 3:
+        T, H, d_qk = q.shape
+        if cu_seqlens is None:
+            if max_seqlen is None:
+                B, N = 1, T
+            else:
+                N = int(max_seqlen)
+                if N <= 0 or T % N:
+                    raise ValueError("fixed-length [T, H, d] input needs T = B * max_seqlen")
+                B = T // N
+        else:
+            if max_seqlen is None:
+                raise ValueError("packed input needs max_seqlen")
+            B = cu_seqlens.numel() - 1
+            N = int(max_seqlen)
+    else:
+        raise ValueError("q must be [B, N, H, d] or [T, H, d]")
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1]:
+        raise ValueError("q, k, v shapes disagree")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    if o is None:
+        o = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    opts = FwdOpts(float(rescale_threshold_log2), int(poly_exp_sixteenths), int(schedule),
+                   stats.data_ptr() if stats is not None else None)
+    st = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), opts)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return o, lse
+
+
+def debug_exp2(x, use_poly: bool, y=None, stream=None):
+    """The kernels' own exp2 (hardware or software cubic) over a fp32 CUDA tensor."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    if y is None:
+        y = torch.empty_like(x)
+    st = int(lib.attn_debug_exp2(x.data_ptr(), y.data_ptr(), x.numel(), int(bool(use_poly)),
+                                 _stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_debug_exp2")
+    return y

@@ -1,0 +1,114 @@
+// C-ABI entry points: argument validation, kernel selection, launch.
+// Declarations and the contract (layouts, ownership, errors) are in
+// include/attn.h.  Every check runs before the first HIP call.
+#include "attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_fwd_kernel.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dims(int d_qk, int d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+}
+
+}  // namespace
+
+extern "C" {
+
+void attn_fwd_opts_default(attn_fwd_opts* opts) {
+  if (!opts) return;
+  opts->rescale_threshold_log2 = 8.0f;
+  opts->poly_exp_sixteenths = 0;
+  opts->schedule = ATTN_SCHEDULE_LONGEST_FIRST;
+  opts->stats = nullptr;
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H or N out of range (B, H >= 1, N >= 0, grid limits)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dims: (d_qk, d_v) must be (64,64), (128,128) or (192,128)";
+    case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes; lse, cu_seqlens 4 bytes";
+    case ATTN_ERR_VALUE: return "invalid value: non-finite scale or option out of range";
+    case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown attn status";
+  }
+}
+
+int attn_version(void) { return kVersion; }
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+                float scale, int causal, hipStream_t stream, const attn_fwd_opts* opts) {
+  attn_fwd_opts def;
+  attn_fwd_opts_default(&def);
+  const attn_fwd_opts& op = opts ? *opts : def;
+
+  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
+  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (!isfinite(op.rescale_threshold_log2)) return ATTN_ERR_VALUE;
+  const int np = op.poly_exp_sixteenths;
+  if (np != 0 && np != 2 && np != 4 && np != 8) return ATTN_ERR_VALUE;
+  if (op.schedule != ATTN_SCHEDULE_LONGEST_FIRST && op.schedule != ATTN_SCHEDULE_NATURAL) return ATTN_ERR_VALUE;
+  if (N == 0) return ATTN_OK;  // no tokens: nothing to do
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return ATTN_ERR_ALIGN;
+  if (!aligned(op.stats, 8)) return ATTN_ERR_ALIGN;
+
+  const int rows = attn::query_block_rows();
+  const int64_t nqb = ((int64_t)N + rows - 1) / rows;
+  if (B > kMaxGridYZ || nqb > kMaxGridYZ) return ATTN_ERR_SHAPE;
+  // token indices are 32-bit inside the kernel
+  if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
+
+  attn::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_qblocks = (int)nqb;
+  float c = fabsf(scale) * 1.44269504088896340736f;
+  if (c < 1e-30f) c = 1e-30f;
+  p.c = c;
+  p.neg_scale = scale < 0.0f ? 1 : 0;
+  p.tau = op.rescale_threshold_log2;
+  p.schedule = op.schedule;
+  p.stats = reinterpret_cast<unsigned long long*>(op.stats);
+
+  const hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, np, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+             float scale, int causal, hipStream_t stream) {
+  return attn_fwd_ex(q, k, v, o, lse, cu_seqlens, B, H, N, d_qk, d_v, scale, causal, stream, nullptr);
+}
+
+int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t stream) {
+  if (n < 0) return ATTN_ERR_SHAPE;
+  if (use_poly != 0 && use_poly != 1) return ATTN_ERR_VALUE;
+  if (n == 0) return ATTN_OK;
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(y, 4)) return ATTN_ERR_ALIGN;
+  const hipError_t err = attn::launch_exp2_debug(x, y, n, use_poly, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

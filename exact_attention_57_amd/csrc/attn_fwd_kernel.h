@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI entry points and the HIP kernels.
+#ifndef EXACT_ATTENTION_57_AMD_ATTN_FWD_KERNEL_H
+#define EXACT_ATTENTION_57_AMD_ATTN_FWD_KERNEL_H
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Kernel arguments (validated by the entry points before any launch).
+struct FwdParams {
+  const uint16_t* q;          // bf16 [T, H, d_qk]
+  const uint16_t* k;          // bf16 [T, H, d_qk]
+  const uint16_t* v;          // bf16 [T, H, d_v]
+  uint16_t* o;                // bf16 [T, H, d_v]
+  float* lse;                 // fp32 [H, T]
+  const int32_t* cu_seqlens;  // device int32 [B+1], or nullptr for fixed length N
+  int B, H, N;
+  int n_qblocks;              // ceil(N / query_block_rows())
+  float c;                    // |scale| * log2(e), at least 1e-30
+  int neg_scale;              // 1: scale < 0, Q is negated on load (exact)
+  float tau;                  // rescale threshold in log2 units; < 0: always rescale
+  int schedule;               // 0: longest-first, 1: natural order
+  unsigned long long* stats;  // optional device counters [4]
+};
+
+int query_block_rows();
+hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int npoly, hipStream_t s);
+hipError_t launch_exp2_debug(const float* x, float* y, int n, int use_poly, hipStream_t s);
+
+}  // namespace attn
+
+#endif

@@ -1,0 +1,131 @@
+/*
+ * attn.h -- C ABI of the fused exact-attention forward pass on MI355X (gfx950).
+ *
+ * Computes, for every packed sequence b, head h and query row i,
+ *
+ *     O[i]   = sum_j softmax_j(scale * q_i . k_j  [j <= i if causal]) v_j
+ *     LSE[i] = ln sum_j exp(scale * q_i . k_j)          (over the same keys)
+ *
+ * i.e. exact softmax attention, evaluated tile by tile with an online softmax
+ * (running row max and row sum, earlier partial results corrected when the
+ * max grows) so the N x N score matrix never reaches HBM.  Sources: the
+ * ainexis.cn deep dive on FlashAttention-4 (background: tiling plus online
+ * softmax; "horizontal extension", concept two: running max / running sum),
+ * jsqmd.com news on FlashAttention-4 (section two: tiles computed on chip).
+ *
+ * Two algorithmic options from the same pages are exposed through
+ * attn_fwd_opts:
+ *   - conditional rescaling (wittx news "FlashAttention-4", section on
+ *     skipping 90% of rescales): the output and row-sum rescale is applied
+ *     only when a tile's row max exceeds the running max by more than a
+ *     threshold in log2 units (8.0 = a factor of 256); the final division by
+ *     the row sum makes the result exact whichever max was kept;
+ *   - software exp2 (wittx, section on faking a hardware instruction in
+ *     software; jsqmd section four, item 1): a fixed fraction of the
+ *     exponentials uses range reduction 2^y = 2^floor(y) * p(y - floor(y))
+ *     with a cubic p evaluated by Horner's rule on FMA, the rest use the
+ *     hardware exp2.
+ * The tile order follows the causal/varlen load-balancing scheduler idea of
+ * the newton.com.tw wiki "FlashAttention-4", core-technology section:
+ * query blocks with the most key tiles are dispatched first.
+ *
+ * ------------------------------------------------------------------ layouts
+ *   q, k : bf16 [T, H, d_qk]   token-major, heads interleaved, contiguous
+ *   v, o : bf16 [T, H, d_v]
+ *   lse  : fp32 [H, T]
+ *   cu_seqlens : NULL for fixed length (T = B*N, sequence b = tokens
+ *                [b*N, (b+1)*N)); otherwise a DEVICE int32 array [B+1] with
+ *                cu[0] = 0, non-decreasing, cu[B] = T, and N >= the longest
+ *                sequence (N sizes the launch grid).  Its contents are a
+ *                precondition and are not validated (that would need a sync).
+ * All pointers are device pointers.  q, k, v, o must be 16-byte aligned;
+ * lse and cu_seqlens 4-byte aligned.
+ *
+ * Supported head dims (d_qk, d_v): (64, 64), (128, 128), (192, 128).
+ * Causal masking is square (query i sees keys j <= i of its own sequence).
+ * scale: any finite value (negative values are handled exactly); when
+ * |scale| * log2(e) < 1e-30 it is raised to 1e-30, which changes no output
+ * (all logits already round to zero) and keeps masked keys at exp2(-inf) = 0.
+ *
+ * ---------------------------------------------------------------- ownership
+ * The caller owns every buffer.  The library never allocates, frees,
+ * retains or synchronises: each call enqueues kernels on `stream` and
+ * returns.  There is no hidden global state besides the kernel code.
+ *
+ * ------------------------------------------------------------------- errors
+ * Every entry point returns ATTN_OK (0) or a negative attn_status.  All
+ * argument checks happen before any HIP call, so a rejected call has no
+ * effect.  ATTN_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ */
+#ifndef EXACT_ATTENTION_57_AMD_ATTN_H
+#define EXACT_ATTENTION_57_AMD_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,         /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,        /* B, H, N out of range or grid too large */
+  ATTN_ERR_UNSUPPORTED = -3,  /* (d_qk, d_v) not one of the supported pairs */
+  ATTN_ERR_ALIGN = -4,        /* pointer misaligned */
+  ATTN_ERR_VALUE = -5,        /* non-finite scale or invalid option value */
+  ATTN_ERR_LAUNCH = -6        /* the HIP launch failed */
+} attn_status;
+
+/* Schedules for the (sequence, head, query-block) work items. */
+#define ATTN_SCHEDULE_LONGEST_FIRST 0  /* causal: query blocks with most key tiles first */
+#define ATTN_SCHEDULE_NATURAL 1        /* query blocks in increasing order */
+
+typedef struct attn_fwd_opts {
+  /* Conditional-rescale threshold in log2 units.  >= 0: rescale a row only
+   * when the tile's row max exceeds the kept max by more than this (0 gives
+   * results bitwise equal to always rescaling).  < 0: always rescale, the
+   * classic online softmax.  Default 8.0 (a factor of 256). */
+  float rescale_threshold_log2;
+  /* Sixteenths of the exponentials computed with the software exp2:
+   * one of 0, 2, 4, 8 (0, 1/8, 1/4, 1/2).  Default 0. */
+  int poly_exp_sixteenths;
+  /* ATTN_SCHEDULE_LONGEST_FIRST (default) or ATTN_SCHEDULE_NATURAL. */
+  int schedule;
+  /* Optional DEVICE uint64[4] the kernel ADDS to (caller zeroes it):
+   * [0] row-tile pairs where a rescale was considered (after a row's first
+   * tile), [1] rescales applied, [2] (wave, tile) pairs computed, [3] work
+   * items (query blocks) that ran.  NULL (default) disables counting. */
+  uint64_t* stats;
+} attn_fwd_opts;
+
+/* Fill *opts with the defaults above. */
+void attn_fwd_opts_default(attn_fwd_opts* opts);
+
+/* Forward pass with default options.  N == 0 is a no-op returning ATTN_OK.
+ * Arguments: see the layouts above; `causal` is 0 or non-zero. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+             float scale, int causal, hipStream_t stream);
+
+/* Forward pass with explicit options (opts == NULL means the defaults). */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+                float scale, int causal, hipStream_t stream, const attn_fwd_opts* opts);
+
+/* Static description of an attn_status value (never NULL). */
+const char* attn_strerror(int status);
+
+/* Test hook: y[i] = the kernels' own exp2 of x[i], n elements of device fp32.
+ * use_poly = 0: hardware exp2 (v_exp_f32); 1: the software range-reduced
+ * cubic.  Same ownership and error rules as attn_fwd (n == 0 is a no-op). */
+int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t stream);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_57_AMD_ATTN_H */

@@ -63,24 +63,27 @@ def _rows_by_sequence(cu: np.ndarray, rows):
 
 
 def attention_f64(q, k, v, cu_seqlens, causal: bool, scale: float, rows=None,
-                  block: int = 1024, widen=None):
+                  block: int = 1024, widen=None, heads=None):
     """Exact attention on float inputs.
 
     q, k: [T, H, d_qk]; v: [T, H, d_v] (any float dtype, or bf16 bit patterns
     when ``widen`` converts them); cu_seqlens: [B+1] token offsets.
     rows: optional strictly increasing global token indices; only those query
     rows are computed (keys still span each row's whole sequence).
+    heads: optional list of head indices to compute (default: all heads).
 
-    Returns (O [R, H, d_v] float64, LSE [H, R] float64), R = len(rows) or T.
+    Returns (O [R, nH, d_v] float64, LSE [nH, R] float64), R = len(rows) or T,
+    nH = len(heads) or H, heads in the order given.
     """
     cvt = widen if widen is not None else (lambda a: np.asarray(a, dtype=np.float64))
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     T, H, d_qk = q.shape
     d_v = v.shape[2]
+    head_list = list(range(H)) if heads is None else [int(x) for x in heads]
     per_seq = _rows_by_sequence(cu, rows)
     R = sum(len(r) for r in per_seq)
-    O = np.empty((R, H, d_v), dtype=np.float64)
-    LSE = np.empty((H, R), dtype=np.float64)
+    O = np.empty((R, len(head_list), d_v), dtype=np.float64)
+    LSE = np.empty((len(head_list), R), dtype=np.float64)
     r0 = 0
     for b, qrows in enumerate(per_seq):
         s, e = int(cu[b]), int(cu[b + 1])
@@ -88,7 +91,7 @@ def attention_f64(q, k, v, cu_seqlens, causal: bool, scale: float, rows=None,
         if n == 0:
             continue
         local = qrows - s                      # query positions within the sequence
-        for h in range(H):
+        for hi, h in enumerate(head_list):
             kb = cvt(k[s:e, h, :])             # [L, d_qk]
             vb = cvt(v[s:e, h, :])             # [L, d_v]
             for c0 in range(0, n, block):
@@ -102,17 +105,17 @@ def attention_f64(q, k, v, cu_seqlens, causal: bool, scale: float, rows=None,
                 m = S.max(axis=1)
                 P = np.exp(S - m[:, None])
                 l = P.sum(axis=1)
-                O[r0 + c0:r0 + c1, h, :] = (P @ vb[:kmax]) / l[:, None]
-                LSE[h, r0 + c0:r0 + c1] = m + np.log(l)
+                O[r0 + c0:r0 + c1, hi, :] = (P @ vb[:kmax]) / l[:, None]
+                LSE[hi, r0 + c0:r0 + c1] = m + np.log(l)
         r0 += n
     return O, LSE
 
 
 def attention(q_bits, k_bits, v_bits, cu_seqlens, causal: bool, scale: float, rows=None,
-              block: int = 1024):
+              block: int = 1024, heads=None):
     """Exact attention on bf16 bit-pattern inputs (uint16 arrays, ``workloads`` layout)."""
     return attention_f64(q_bits, k_bits, v_bits, cu_seqlens, causal, scale, rows=rows,
-                         block=block, widen=bf16_bits_to_f64)
+                         block=block, widen=bf16_bits_to_f64, heads=heads)
 
 
 def attention_probs_f64(q, k, causal: bool, scale: float):

@@ -115,3 +115,40 @@ def test_pages_threshold_constant():
     lo, hi = GOLDEN["poly_emulated_fraction"]["lo"], GOLDEN["poly_emulated_fraction"]["hi"]
     # the kernel's emulated fractions 1/8 and 1/4 fall in the pages' range
     assert lo <= 1 / 8 <= hi and lo <= 1 / 4 <= hi
+
+
+# ------------------------------------------------------------------ GPU: the kernels' exp2
+
+@pytest.mark.gpu
+def test_kernel_exp2_against_exact(fit):
+    """attn_debug_exp2 runs the kernels' own exp2 routines on the GPU."""
+    import torch
+    import exact_attention_57_amd as ea
+    coeffs, E = fit
+    rng = np.random.default_rng(2)
+    y = np.concatenate([rng.uniform(-16, 0, 1_000_000), rng.uniform(-126, 8, 1_000_000),
+                        np.arange(-126, 9), [0.0, -0.0, 1e-7, -1e-7]]).astype(np.float32)
+    x = torch.from_numpy(y).cuda()
+    hw = ea.debug_exp2(x, False).cpu().numpy().astype(np.float64)
+    sw = ea.debug_exp2(x, True).cpu().numpy().astype(np.float64)
+    exact = np.exp2(y.astype(np.float64))
+    rel_hw = np.abs(hw / exact - 1)
+    rel_sw = np.abs(sw / exact - 1)
+    print(f"hw max rel {rel_hw.max():.3e}; sw max rel {rel_sw.max():.3e} (fit level {E:.3e})")
+    assert rel_hw.max() <= 2.0 ** -21
+    assert rel_sw.max() <= E + 4 * 2.0 ** -24
+    ints = np.arange(-126, 9).astype(np.float32)
+    sel = np.isin(y, ints) & (np.abs(y) >= 1)
+    assert np.array_equal(sw[sel], exact[sel])          # exact at integers (c0 = 1)
+    # agreement with the oracle's independent fit run through the same fp32 steps
+    ref = exp2_poly_f32(y, coeffs).astype(np.float64)
+    assert np.max(np.abs(sw / ref - 1)) <= 1e-6
+    # bf16 agreement with the exact exponential (pages: about 99%)
+    lo = (y >= -16) & (y <= 0)
+    rate = float(np.mean(round_bf16_f64(sw[lo]) == round_bf16_f64(exact[lo])))
+    print(f"bf16 agreement of the kernel's cubic with exact exp2 on [-16, 0]: {rate:.4f}")
+    assert rate >= 0.985
+    # masked keys: exp2(-inf) is 0 on the hardware path and below 2^-126 on the software path
+    z = torch.tensor([-np.inf], dtype=torch.float32, device="cuda")
+    assert ea.debug_exp2(z, False).item() == 0.0
+    assert 0.0 <= ea.debug_exp2(z, True).item() < 2.0 ** -126

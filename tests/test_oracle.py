@@ -285,3 +285,11 @@ def test_pins_catch_planted_mistakes(monkeypatch, plant):
     Om, Lm = _brute_force_mp(q[:, 0], k[:, 0], v[:, 0], True, 0.9)
     err = max(np.max(np.abs(O[:, 0] - Om)), np.max(np.abs(L[0] - Lm)))
     assert err > 1e-6, "a planted mistake went unnoticed by the brute-force pin"
+
+
+def test_head_subset_matches_full():
+    T, H = 40, 4
+    q, k, v = _rand(T, H, 8), _rand(T, H, 8), _rand(T, H, 8)
+    O, L = attention_f64(q, k, v, _cu([T]), True, 0.5)
+    Os, Ls = attention_f64(q, k, v, _cu([T]), True, 0.5, heads=[3, 1])
+    assert np.array_equal(Os, O[:, [3, 1]]) and np.array_equal(Ls, L[[3, 1]])

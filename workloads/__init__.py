@@ -7,9 +7,12 @@ may use it without sharing any of the method.
 
 bf16 tensors are returned as ``numpy.uint16`` arrays holding the raw bf16
 bit patterns (numpy has no bf16 type).  Values are drawn in float32 with
-``numpy.random.default_rng(seed)`` (PCG64) and rounded to bf16 with
-round-to-nearest-even.  Draw order per workload: sequence lengths (packed
-workload only), then Q, K, V, each with ``standard_normal(dtype=float32)``.
+``standard_normal(dtype=float32)`` from PCG64 generators and rounded to bf16
+with round-to-nearest-even.  Sequence lengths (packed workload) come from
+``numpy.random.default_rng(seed)``; Q, K, V are streams 0, 1, 2, each cut
+into chunks of about 2^20 elements drawn from
+``default_rng(SeedSequence(seed, spawn_key=(stream, chunk)))`` so that
+threads can fill them in parallel with the same result.
 
 Layouts: q, k are ``[T, H, d_qk]``, v is ``[T, H, d_v]`` (token-major, heads
 interleaved), where T is the total token count; ``cu_seqlens`` is int32
@@ -18,6 +21,9 @@ interleaved), where T is the total token count; ``cu_seqlens`` is int32
 from __future__ import annotations
 
 import math
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -112,36 +118,53 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-class _Chunker:
-    """Reusable float32/uint32 chunk buffers for drawing and rounding."""
-
-    def __init__(self, elems: int):
-        self.f = np.empty(elems, dtype=np.float32)
-        self.s = np.empty(elems, dtype=np.uint32)
-
-    def fill(self, rng, out2d: np.ndarray, add_rows: np.ndarray | None = None):
-        """Fill uint16 [rows, cols] with bf16(N(0,1) + add_rows[row])."""
-        rows, cols = out2d.shape
-        per = max(1, self.f.size // max(cols, 1))
-        for t0 in range(0, rows, per):
-            t1 = min(rows, t0 + per)
-            n = (t1 - t0) * cols
-            z = self.f[:n].reshape(t1 - t0, cols)
-            rng.standard_normal(dtype=np.float32, out=z)
-            if add_rows is not None:
-                z += add_rows[t0:t1, None].astype(np.float32)
-            f32_to_bf16_bits(z, out=out2d[t0:t1], scratch=self.s[:n])
+_CHUNK_ELEMS = 1 << 20
+_TLS = threading.local()
 
 
-_CHUNK_ELEMS = 1 << 22
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
-def _normal_bf16(rng: np.random.Generator, shape, chunker=None) -> np.ndarray:
-    """N(0,1) float32 draws rounded to bf16, generated in chunks to bound memory."""
+def _fill_normal(out2d: np.ndarray, seed: int, stream: int, add_rows: np.ndarray | None = None):
+    """Fill uint16 [rows, cols] with bf16(N(0,1) + add_rows[row]).
+
+    Rows are cut into chunks of about 2^20 elements; chunk c of stream s is
+    drawn from ``default_rng(SeedSequence(seed, spawn_key=(s, c)))``, so the
+    values do not depend on how many threads fill them.
+    """
+    rows, cols = out2d.shape
+    per = max(1, _CHUNK_ELEMS // max(cols, 1))
+    starts = list(range(0, rows, per))
+
+    def work(ci):
+        t0 = starts[ci]
+        t1 = min(rows, t0 + per)
+        n = (t1 - t0) * cols
+        buf = getattr(_TLS, "f", None)
+        if buf is None or buf.size < per * cols:
+            _TLS.f = buf = np.empty(per * cols, dtype=np.float32)
+            _TLS.s = np.empty(per * cols, dtype=np.uint32)
+        z = buf[:n].reshape(t1 - t0, cols)
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(stream, ci)))
+        rng.standard_normal(dtype=np.float32, out=z)
+        if add_rows is not None:
+            z += add_rows[t0:t1, None]
+        f32_to_bf16_bits(z, out=out2d[t0:t1], scratch=_TLS.s[:n])
+
+    if len(starts) <= 1:
+        for ci in range(len(starts)):
+            work(ci)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(len(starts))))
+
+
+def _normal_bf16(seed: int, stream: int, shape, add_rows=None) -> np.ndarray:
     T = shape[0]
     row = int(np.prod(shape[1:]))
     out = np.empty((T, row), dtype=np.uint16)
-    (chunker or _Chunker(_CHUNK_ELEMS)).fill(rng, out)
+    _fill_normal(out, seed, stream, add_rows)
     return out.reshape(shape)
 
 
@@ -156,13 +179,6 @@ def ramp_strength(d: int) -> float:
     """
     del d
     return 13.255
-
-
-def _ramp_bf16(rng, L: int, H: int, d: int, coef_rows: np.ndarray, chunker=None):
-    """bf16(N(0,1) + coef_rows[t]) for every element of token t, shape [L, H, d]."""
-    out = np.empty((L, H * d), dtype=np.uint16)
-    (chunker or _Chunker(_CHUNK_ELEMS)).fill(rng, out, add_rows=coef_rows)
-    return out.reshape(L, H, d)
 
 
 def make_inputs(wl, seed: int = 0) -> dict:
@@ -183,30 +199,18 @@ def make_inputs(wl, seed: int = 0) -> dict:
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
     H = wl.H
+    qadd = kadd = None
     if wl.ramp:
         beta = ramp_strength(wl.d_qk)
         u = 1.0 / math.sqrt(wl.d_qk)
-        ch = _Chunker(_CHUNK_ELEMS)
-        qs, ks, vs = [], [], []
-        # Q for all sequences, then K, then V (the draw order of the module doc).
+        qadd = np.full(T, beta * u, dtype=np.float32)
+        kadd = np.empty(T, dtype=np.float32)
         for b in range(wl.B):
             L = int(lengths[b])
-            qs.append(_ramp_bf16(rng, L, H, wl.d_qk, np.full(L, beta * u), ch))
-        for b in range(wl.B):
-            L = int(lengths[b])
-            t = np.arange(L, dtype=np.float64) / max(L - 1, 1)
-            ks.append(_ramp_bf16(rng, L, H, wl.d_qk, beta * t * u, ch))
-        for b in range(wl.B):
-            L = int(lengths[b])
-            vs.append(_normal_bf16(rng, (L, H, wl.d_v), ch))
-        q = np.concatenate(qs, axis=0)
-        k = np.concatenate(ks, axis=0)
-        v = np.concatenate(vs, axis=0)
-    else:
-        ch = _Chunker(_CHUNK_ELEMS)
-        q = _normal_bf16(rng, (T, H, wl.d_qk), ch)
-        k = _normal_bf16(rng, (T, H, wl.d_qk), ch)
-        v = _normal_bf16(rng, (T, H, wl.d_v), ch)
+            kadd[cu[b]:cu[b + 1]] = beta * u * np.arange(L, dtype=np.float64) / max(L - 1, 1)
+    q = _normal_bf16(seed, 0, (T, H, wl.d_qk), qadd)
+    k = _normal_bf16(seed, 1, (T, H, wl.d_qk), kadd)
+    v = _normal_bf16(seed, 2, (T, H, wl.d_v))
     return dict(q=q, k=k, v=v, cu_seqlens=cu.astype(np.int32), lengths=lengths,
                 B=wl.B, H=H, N=int(lengths.max()) if wl.B else 0, d_qk=wl.d_qk, d_v=wl.d_v,
                 causal=wl.causal, scale=wl.softmax_scale(), T=T, key=wl.key)
@@ -220,18 +224,20 @@ def make_custom_inputs(lengths, H: int, d_qk: int, d_v: int, seed: int = 0,
     any tile size, single-token sequences.
     """
     lengths = np.asarray(lengths, dtype=np.int64)
-    rng = np.random.default_rng(seed)
     cu = np.zeros(len(lengths) + 1, dtype=np.int64)
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
 
-    def draw(d):
-        x = rng.standard_normal((T, H, d), dtype=np.float32) * np.float32(std) + np.float32(mean)
+    def draw(stream, d):
+        bits = _normal_bf16(seed, stream, (T, H, d))
+        if std == 1.0 and mean == 0.0:
+            return bits
+        x = bf16_bits_to_f32(bits) * np.float32(std) + np.float32(mean)
         return f32_to_bf16_bits(x)
 
-    q = draw(d_qk)
-    k = draw(d_qk)
-    v = draw(d_v)
+    q = draw(0, d_qk)
+    k = draw(1, d_qk)
+    v = draw(2, d_v)
     return dict(q=q, k=k, v=v, cu_seqlens=cu.astype(np.int32), lengths=lengths,
                 B=len(lengths), H=H, N=int(lengths.max()) if len(lengths) else 0,
                 d_qk=d_qk, d_v=d_v, T=T)
