@@ -15,7 +15,7 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "lib", "fwd", "fwd_raw", "debug_exp2", "strerror", "version",
+    "AttnError", "lib", "fwd", "fwd_raw", "debug_exp2", "strerror", "version", "geometry",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
     "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
     "SUPPORTED_DIMS", "LIB_PATH",
@@ -89,6 +89,8 @@ def _load():
     L.attn_debug_exp2.restype = i32
     L.attn_version.argtypes = []
     L.attn_version.restype = i32
+    L.attn_fwd_geometry.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.attn_fwd_geometry.restype = i32
     return L
 
 
@@ -101,6 +103,15 @@ def strerror(status: int) -> str:
 
 def version() -> int:
     return int(lib.attn_version())
+
+
+def geometry(d_qk: int, d_v: int) -> dict:
+    """Work decomposition of the forward kernels: rows per work item, keys per tile, rows per wave."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = int(lib.attn_fwd_geometry(int(d_qk), int(d_v), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_geometry")
+    return {"rows_per_item": a.value, "keys_per_tile": b.value, "rows_per_wave": c.value}
 
 
 def default_opts() -> FwdOpts:

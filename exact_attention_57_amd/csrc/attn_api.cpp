@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -45,6 +45,14 @@ const char* attn_strerror(int status) {
 }
 
 int attn_version(void) { return kVersion; }
+
+int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile, int* rows_per_wave) {
+  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
+  if (rows_per_item) *rows_per_item = attn::query_block_rows();
+  if (keys_per_tile) *keys_per_tile = attn::keys_per_tile();
+  if (rows_per_wave) *rows_per_wave = attn::rows_per_wave();
+  return ATTN_OK;
+}
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,

@@ -1,13 +1,16 @@
 // Fused exact-attention forward kernels for gfx950 (CDNA4, MI355X).
 //
-// One workgroup = 4 wave64s = one query block of 128 rows of one (sequence,
-// head); each wave owns 32 query rows for the whole key loop.  Per key tile of
-// 64 keys the workgroup stages K (row-major) and V (transposed, V^T) in LDS;
-// each wave then computes
+// One workgroup = 8 wave64s (two per SIMD) = one query block of 256 rows of
+// one (sequence, head); each wave owns 32 query rows for the whole key loop.
+// Key tiles of 64 keys are staged row-major in LDS (K and V, two stages: the
+// next tile's global loads are in flight while the current tile is used); each
+// wave then computes
 //
 //   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulators (Q^T resident in VGPRs)
 //   online softmax   row max / conditional rescale / exp2 / row sum, in fp32
-//   O^T += V^T P^T   bf16 MFMA 32x32x16, fp32 accumulators
+//   O^T += V^T P^T   bf16 MFMA 32x32x16, fp32 accumulators; the V^T operand
+//                    comes straight from the row-major V tile through the
+//                    gfx950 transposing LDS read (ds_read_b64_tr_b16)
 //
 // Computing the transposed score block puts one query row in each lane (lane
 // l and lane l^32 hold the two halves of the row's keys), so the row max and
@@ -47,11 +50,18 @@ constexpr float kExp2C2 = 0x1.d236c6p-3f;   // 0.227643535
 constexpr float kExp2C3 = 0x1.3babb0p-4f;   // 0.0770680308
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;              // 2 waves per SIMD
 constexpr int kThreads = kWave * kWaves;
-constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
+constexpr int kRowsPerWave = 32;
+constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per tile
 constexpr int kKeyBlocks = kBlockN / 32;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
 __device__ __forceinline__ float exp2_hw(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
@@ -86,21 +96,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// LDS tile layouts (bf16 elements, row-major, padded rows):
+//  K tile [kBlockN][DQK + 8]: the 16-byte pad shifts consecutive rows by 4
+//    banks, so the 16 rows one ds_read_b128 phase touches (same column chunk)
+//    land in 16 distinct 4-bank groups.
+//  V tile [kBlockN][DV + 32]: the 64-byte pad shifts consecutive rows by 16
+//    banks, so the 4 rows x 64 bytes a half-wave of ds_read_b64_tr_b16 reads
+//    cover all 64 banks once.
+template <int DQK, int DV>
+struct TileLayout {
+  static constexpr int K_PITCH = DQK + 8;
+  static constexpr int V_PITCH = DV + 32;
+  static constexpr int K_ELEMS = kBlockN * K_PITCH;
+  static constexpr int V_ELEMS = kBlockN * V_PITCH;
+  static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int K_CHUNKS = kBlockN * DQK / 8;   // 16-byte chunks per K tile
+  static constexpr int V_CHUNKS = kBlockN * DV / 8;
+  static constexpr int K_LOADS = (K_CHUNKS + kThreads - 1) / kThreads;
+  static constexpr int V_LOADS = (V_CHUNKS + kThreads - 1) / kThreads;
+};
+
 template <int DQK, int DV, bool CAUSAL, int NPOLY>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
+  using Lay = TileLayout<DQK, DV>;
   constexpr int QK_STEPS = DQK / 16;             // MFMA k-steps for S^T
   constexpr int D_BLOCKS = DV / 32;              // 32-row blocks of O^T
-  constexpr int K_PITCH = DQK + 8;               // bf16 elements per K row in LDS (16 B pad)
-  constexpr int VT_PITCH = kBlockN + 8;          // bf16 elements per V^T row in LDS
-  constexpr int K_CHUNKS = kBlockN * DQK / 8;    // 16-byte chunks per K tile
-  constexpr int K_LOADS = (K_CHUNKS + kThreads - 1) / kThreads;
-  constexpr int V_DGROUPS = DV / 8;              // V staged as 4-key x 8-d blocks
-  constexpr int V_BLOCKS = (kBlockN / 4) * V_DGROUPS;
-  constexpr int V_LOADS = (V_BLOCKS + kThreads - 1) / kThreads;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlockN * K_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VT_PITCH];
+  // two stages, each holding one K tile and one V tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Lay::STAGE_ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -133,8 +157,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   const uint16_t* __restrict__ kbase = p.k + (int64_t)seq0 * qk_row + (int64_t)h * DQK;
   const uint16_t* __restrict__ vbase = p.v + (int64_t)seq0 * v_row + (int64_t)h * DV;
 
-  const int qw0 = q0 + 32 * wave;        // first query row of this wave
-  const int qrow = qw0 + lq;             // this lane's query row (position in the sequence)
+  const int qw0 = q0 + kRowsPerWave * wave;   // first query row of this wave
+  const int qrow = qw0 + lq;                  // this lane's query row (position in the sequence)
   const bool row_valid = qrow < L;
 
   // ---- Q^T operand, resident for the whole key loop.  Lane (g, lq) holds
@@ -153,61 +177,51 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- staging registers for the next K/V tile (global -> VGPR -> LDS)
-  u32x4_t kst[K_LOADS];
-  u32x4_t vst[V_LOADS][4];
+  u32x4_t kst[Lay::K_LOADS];
+  u32x4_t vst[Lay::V_LOADS];
 
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
+    for (int i = 0; i < Lay::K_LOADS; ++i) {
       const int c = i * kThreads + tid;
       const int row = c / (DQK / 8);
       const int col8 = c % (DQK / 8);
       const int key = k0 + row;
       u32x4_t val = {0u, 0u, 0u, 0u};
-      if (c < K_CHUNKS && key < L) val = *(const u32x4_t*)(kbase + (int64_t)key * qk_row + col8 * 8);
+      if (c < Lay::K_CHUNKS && key < L) val = *(const u32x4_t*)(kbase + (int64_t)key * qk_row + col8 * 8);
       kst[i] = val;
     }
 #pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int blk = i * kThreads + tid;
-      const int dg = blk % V_DGROUPS;
-      const int kg = blk / V_DGROUPS;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = k0 + 4 * kg + kk;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (blk < V_BLOCKS && key < L) val = *(const u32x4_t*)(vbase + (int64_t)key * v_row + dg * 8);
-        vst[i][kk] = val;
-      }
+    for (int i = 0; i < Lay::V_LOADS; ++i) {
+      const int c = i * kThreads + tid;
+      const int row = c / (DV / 8);
+      const int col8 = c % (DV / 8);
+      const int key = k0 + row;
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (c < Lay::V_CHUNKS && key < L) val = *(const u32x4_t*)(vbase + (int64_t)key * v_row + col8 * 8);
+      vst[i] = val;
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    lds_u16_t* ks_ = (lds_u16_t*)smem + stage * Lay::STAGE_ELEMS;
+    lds_u16_t* vs_ = ks_ + Lay::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
+    for (int i = 0; i < Lay::K_LOADS; ++i) {
       const int c = i * kThreads + tid;
-      if (c < K_CHUNKS) {
+      if (c < Lay::K_CHUNKS) {
         const int row = c / (DQK / 8);
         const int col8 = c % (DQK / 8);
-        *(u32x4_t*)(&Ks[row * K_PITCH + col8 * 8]) = kst[i];
+        *(lds_u32x4_t*)(ks_ + row * Lay::K_PITCH + col8 * 8) = kst[i];
       }
     }
 #pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int blk = i * kThreads + tid;
-      if (blk < V_BLOCKS) {
-        const int dg = blk % V_DGROUPS;
-        const int kg = blk / V_DGROUPS;
-        // 4 keys x 8 d  ->  8 rows of V^T with 4 consecutive keys each
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int w = j / 2;
-          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-          u32x2_t out;
-          out.x = __builtin_amdgcn_perm(vst[i][1][w], vst[i][0][w], sel);
-          out.y = __builtin_amdgcn_perm(vst[i][3][w], vst[i][2][w], sel);
-          *(u32x2_t*)(&Vt[(dg * 8 + j) * VT_PITCH + 4 * kg]) = out;
-        }
+    for (int i = 0; i < Lay::V_LOADS; ++i) {
+      const int c = i * kThreads + tid;
+      if (c < Lay::V_CHUNKS) {
+        const int row = c / (DV / 8);
+        const int col8 = c % (DV / 8);
+        *(lds_u32x4_t*)(vs_ + row * Lay::V_PITCH + col8 * 8) = vst[i];
       }
     }
   };
@@ -225,121 +239,135 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
   bool first = true;
 
-  // Key offset (within a 32-key block) of accumulator register r in lane half
-  // g: the K rows are loaded in the order sigma(m) = m with bits 2 and 3
-  // swapped, which makes registers 0..7 (and 8..15) hold 8 consecutive keys
-  // -- exactly the B-operand slots of the second product.
+  // K rows are read in the order sigma(m) = m with bits 2 and 3 swapped: then
+  // accumulator registers 0..7 (and 8..15) of a 32-key block hold 8
+  // consecutive keys -- exactly the B-operand slots of the second product.
+  const int sig = (lq & ~0xC) | ((lq & 4) << 1) | ((lq & 8) >> 1);
+  // ds_read_b64_tr_b16 source addressing for the V^T operand: in each group of
+  // 16 lanes, lane s reads 4 consecutive d-values of key row s/4; the
+  // transpose hands lane i the values of 4 consecutive keys at d-column i.
+  const int grp = lane / 16;
+  const int sl = lane % 16;
+  const int v_key_off = 8 * (grp / 2) + sl / 4;
+  const int v_col_off = 16 * (grp % 2) + 4 * (sl % 4);
+
   load_tile(0);
+  store_tile(0);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * kBlockN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
+    const int stage = t & 1;
     if (t + 1 < ntiles) load_tile(k0 + kBlockN);
 
-    if (CAUSAL && k0 > qw0 + 31) continue;   // every key of the tile is above this wave's rows
-    ++n_tiles;
+    if (!CAUSAL || k0 <= qw0 + kRowsPerWave - 1) {   // else: every key is above this wave's rows
+      ++n_tiles;
+      const lds_u16_t* ks_ = (const lds_u16_t*)smem + stage * Lay::STAGE_ELEMS;
+      const lds_u16_t* vs_ = ks_ + Lay::K_ELEMS;
 
-    // ---- S^T = K Q^T
-    f32x16_t sacc[kKeyBlocks];
+      // ---- S^T = K Q^T
+      f32x16_t sacc[kKeyBlocks];
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-    {
-      const int m = lq;
-      const int sig = (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < QK_STEPS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < kKeyBlocks; ++kb) {
-          const bf16x8_t a = *(const bf16x8_t*)(&Ks[(kb * 32 + sig) * K_PITCH + 16 * ks + 8 * g]);
+          const bf16x8_t a = *(const lds_bf16x8_t*)(ks_ + (kb * 32 + sig) * Lay::K_PITCH + 16 * ks + 8 * g);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
       }
-    }
 
-    // ---- mask (only tiles that reach past the sequence end or this wave's diagonal)
-    const bool need_mask = (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
+      // ---- mask (only tiles that reach past the sequence end or this wave's diagonal)
+      const bool need_mask = (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+            if (key > lim) sacc[kb][r] = -__builtin_inff();
+          }
+      }
+
+      // ---- row max of this tile (raw logits; c > 0 so max commutes with scaling)
+      float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-          if (key > lim) sacc[kb][r] = -__builtin_inff();
-        }
-    }
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sacc[kb][r]);
+      mx = max_with_partner(mx);
+      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
 
-    // ---- row max of this tile (raw logits; c > 0 so max commutes with scaling)
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sacc[kb][r]);
-    mx = max_with_partner(mx);
-    const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-
-    // ---- conditional rescale
-    if (first) {
-      m_run = m_tile;   // O and l are still zero: nothing to rescale
-      first = false;
-    } else {
-      bool need;
-      float m_new;
-      if (tau < 0.0f) {                 // classic online softmax: always rescale
-        m_new = __builtin_fmaxf(m_run, m_tile);
-        need = true;
+      // ---- conditional rescale
+      if (first) {
+        m_run = m_tile;   // O and l are still zero: nothing to rescale
+        first = false;
       } else {
-        need = m_tile > m_run + tau;
-        m_new = need ? m_tile : m_run;
-      }
-      if (row_valid && g == 0) {
-        n_considered += 1;
-        n_taken += need ? 1u : 0u;
-      }
-      if (tau < 0.0f || __builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
+        bool need;
+        float m_new;
+        if (tau < 0.0f) {                 // classic online softmax: always rescale
+          m_new = __builtin_fmaxf(m_run, m_tile);
+          need = true;
+        } else {
+          need = m_tile > m_run + tau;
+          m_new = need ? m_tile : m_run;
+        }
+        if (row_valid && g == 0) {
+          n_considered += 1;
+          n_taken += need ? 1u : 0u;
+        }
+        if (tau < 0.0f || __builtin_amdgcn_ballot_w64(need) != 0) {
+          const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
 #pragma unroll
-        for (int db = 0; db < D_BLOCKS; ++db)
+          for (int db = 0; db < D_BLOCKS; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        l_part *= alpha;
-        m_run = m_new;
-      }
-    }
-
-    // ---- P = exp2(c*s - m), row sum, bf16 B operand
-    u32x4_t pb[kKeyBlocks][2];
-    const float neg_m = -m_run;
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
-        pv[r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
-        l_part += pv[r];
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb[kb][hh][j] = pack_bf16x2(pv[8 * hh + 2 * j], pv[8 * hh + 2 * j + 1]);
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb[kb][hh]);
-#pragma unroll
-        for (int db = 0; db < D_BLOCKS; ++db) {
-          const bf16x8_t a = *(const bf16x8_t*)(&Vt[(db * 32 + lq) * VT_PITCH + kb * 32 + 16 * hh + 8 * g]);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[db], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          l_part *= alpha;
+          m_run = m_new;
         }
       }
+
+      // ---- P = exp2(c*s - m), row sum, bf16 B operand
+      u32x4_t pb[kKeyBlocks][2];
+      const float neg_m = -m_run;
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb) {
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
+          pv[r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
+          l_part += pv[r];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pb[kb][hh][j] = pack_bf16x2(pv[8 * hh + 2 * j], pv[8 * hh + 2 * j + 1]);
+      }
+
+      // ---- O^T += V^T P^T  (V^T operand by transposing LDS reads)
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb[kb][hh]);
+          const lds_u16_t* vrow = vs_ + (kb * 32 + 16 * hh + v_key_off) * Lay::V_PITCH + v_col_off;
+#pragma unroll
+          for (int db = 0; db < D_BLOCKS; ++db) {
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + db * 32));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + 4 * Lay::V_PITCH + db * 32));
+            const i16x4_t both[2] = {lo, hi};
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[db], 0, 0, 0);
+          }
+        }
+    }
+
+    if (t + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2
@@ -401,6 +429,8 @@ static hipError_t launch_dims(const FwdParams& p, bool causal, int npoly, hipStr
 }
 
 int query_block_rows() { return kBlockM; }
+int keys_per_tile() { return kBlockN; }
+int rows_per_wave() { return kRowsPerWave; }
 
 hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int npoly, hipStream_t s) {
   if (d_qk == 64 && d_v == 64) return launch_dims<64, 64>(p, causal, npoly, s);

@@ -121,6 +121,13 @@ const char* attn_strerror(int status);
  * cubic.  Same ownership and error rules as attn_fwd (n == 0 is a no-op). */
 int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t stream);
 
+/* Work decomposition the forward kernels use for a head-dim pair, needed to
+ * interpret the statistics counters: *rows_per_item query rows per work
+ * item, *keys_per_tile keys per K/V tile, *rows_per_wave query rows per
+ * wave64.  Any output pointer may be NULL.  Returns ATTN_OK, or
+ * ATTN_ERR_UNSUPPORTED for an unsupported (d_qk, d_v).  No HIP call. */
+int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile, int* rows_per_wave);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int attn_version(void);
 

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("attn_fwd", "attn_fwd_ex", "attn_fwd_opts_default", "attn_strerror",
-                 "attn_debug_exp2", "attn_version"):
+                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry"):
         assert want in names
 
 
@@ -71,7 +71,7 @@ def call(**kw):
     (dict(H=0), ea.ATTN_ERR_SHAPE),
     (dict(N=-1), ea.ATTN_ERR_SHAPE),
     (dict(B=70000), ea.ATTN_ERR_SHAPE),
-    (dict(N=65536 * 128 + 1), ea.ATTN_ERR_SHAPE),
+    (dict(N=65535 * ea.geometry(128, 128)["rows_per_item"] + 1), ea.ATTN_ERR_SHAPE),
     (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=128, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
@@ -113,3 +113,12 @@ def test_debug_exp2_validation():
     assert f(None, P, 4, 0, None) == ea.ATTN_ERR_NULL
     assert f(P + 2, P, 4, 0, None) == ea.ATTN_ERR_ALIGN
     assert f(None, None, 0, 1, None) == ea.ATTN_OK
+
+
+def test_geometry_query():
+    for d_qk, d_v in ea.SUPPORTED_DIMS:
+        g = ea.geometry(d_qk, d_v)
+        assert g["rows_per_item"] % g["rows_per_wave"] == 0
+        assert g["keys_per_tile"] % 32 == 0
+    with pytest.raises(ea.AttnError):
+        ea.geometry(96, 96)

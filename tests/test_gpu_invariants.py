@@ -156,9 +156,13 @@ def test_guard_regions_untouched():
         assert bool((lbuf[:guard] == -7.25).all()) and bool((lbuf[-guard:] == -7.25).all())
 
 
-def expected_counts(lengths, causal, H, block_m=128, tile=64, waves=4):
+def expected_counts(lengths, causal, H, d=128):
     """Closed forms for the statistics counters: wave-tiles computed, work items, and the
     number of (valid row, tile) pairs after each row's first tile, over H heads."""
+    import exact_attention_57_amd as ea
+    geo = ea.geometry(d, d)
+    block_m, tile, rw = geo["rows_per_item"], geo["keys_per_tile"], geo["rows_per_wave"]
+    waves = block_m // rw
     tiles = items = considered = 0
     for L in lengths:
         for q0 in range(0, L, block_m):
@@ -166,10 +170,10 @@ def expected_counts(lengths, causal, H, block_m=128, tile=64, waves=4):
             kend = min(L, q0 + block_m) if causal else L
             nt = -(-kend // tile)
             for w in range(waves):
-                qw0 = q0 + 32 * w
-                done = sum(1 for t in range(nt) if (not causal) or t * tile <= qw0 + 31)
+                qw0 = q0 + rw * w
+                done = sum(1 for t in range(nt) if (not causal) or t * tile <= qw0 + rw - 1)
                 tiles += done
-                valid_rows = max(0, min(32, L - qw0))
+                valid_rows = max(0, min(rw, L - qw0))
                 considered += valid_rows * (done - 1)
     return tiles * H, items * H, considered * H
 
@@ -189,8 +193,10 @@ def test_statistics_match_closed_forms_and_oracle_model(causal):
         qf = workloads.bf16_bits_to_f32(inp["q"]).astype(np.float64)
         kf = workloads.bf16_bits_to_f32(inp["k"]).astype(np.float64)
         vf = workloads.bf16_bits_to_f32(inp["v"]).astype(np.float64)
+        import exact_attention_57_amd as ea
+        tile = ea.geometry(128, 128)["keys_per_tile"]
         _, _, ost = oracle.online_softmax_attention_f64(qf, kf, vf, inp["cu_seqlens"], causal,
-                                                        inp["scale"], tau=tau, tile=64)
+                                                        inp["scale"], tau=tau, tile=tile)
         say(f"  tau={tau} causal={causal}: gpu taken {st[1]} / considered {st[0]}; "
             f"oracle model taken {ost['taken']} / {ost['considered']}")
         assert ost["considered"] == considered
