@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB 5 times (for scaling "
+                         "FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -137,6 +140,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return
 
     import exact_attention_57_amd as ea
     import workloads
