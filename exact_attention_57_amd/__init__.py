@@ -21,7 +21,10 @@ __all__ = [
     "SUPPORTED_DIMS", "LIB_PATH",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# EXACT_ATTENTION_57_AMD_LIB may point at another build of the same library
+# (e.g. a variant compiled with different tile settings) for comparisons.
+LIB_PATH = os.environ.get("EXACT_ATTENTION_57_AMD_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_OK = 0
 ATTN_ERR_NULL = -1

@@ -2,9 +2,7 @@
 //
 // One workgroup = 8 wave64s (two per SIMD) = one query block of 256 rows of
 // one (sequence, head); each wave owns 32 query rows for the whole key loop.
-// Key tiles of 64 keys are staged row-major in LDS (K and V, two stages: the
-// next tile's global loads are in flight while the current tile is used); each
-// wave then computes
+// Per key tile of 64 keys each wave computes
 //
 //   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulators (Q^T resident in VGPRs)
 //   online softmax   row max / conditional rescale / exp2 / row sum, in fp32
@@ -18,10 +16,25 @@
 // a per-lane scalar, and the fp32 S^T accumulator -- rounded to bf16 -- is
 // already the B operand of the second product: P never leaves the registers.
 //
+// Ping-pong schedule.  Waves 0-3 (group 0) and 4-7 (group 1) share the four
+// SIMDs, one of each per SIMD.  Time is cut into phases separated by
+// workgroup barriers; in a group's "matrix" phase for tile j it runs the
+// output product of tile j-1 and the score product of tile j (all MFMA), in
+// its "softmax" phase it runs the softmax of tile j (VALU).  Group 1 runs one
+// phase behind group 0, so on every SIMD one wave feeds the matrix core while
+// the other computes exponentials.
+//
+// LDS: two K and two V tile buffers (dense rows, XOR-swizzled 16-byte chunks),
+// filled straight from HBM by buffer_load ... lds at the start of each even
+// phase for the tiles needed two phases later.
+//
 // Method sources (web pages on FlashAttention-4):
 //  * tiling + online softmax with running max/sum: ainexis.cn deep dive,
 //    background section and "horizontal extension" concept two; jsqmd news,
 //    section two.
+//  * overlap of matrix products with softmax and loads (one part multiplies
+//    while another does softmax and another loads): jsqmd news section four,
+//    item 2; newton.com.tw wiki "FlashAttention-4", core-technology section.
 //  * conditional rescaling with threshold 8 in log2 units (factor 256), exact
 //    after the final normalisation: wittx news "FlashAttention-4", section on
 //    skipping 90% of rescales.
@@ -35,12 +48,23 @@
 
 #include "attn_fwd_kernel.h"
 
+#ifndef ATTN_SETPRIO
+#define ATTN_SETPRIO 1  // raise the issue priority of the wave in its matrix phase
+#endif
+
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
 // Cubic p(r) = 1 + C1 r + C2 r^2 + C3 r^3 minimising max |p(r)/2^r - 1| on
 // [0, 1] (relative minimax, max error 8.56e-5), rounded to fp32.  Derived by
@@ -50,18 +74,12 @@ constexpr float kExp2C2 = 0x1.d236c6p-3f;   // 0.227643535
 constexpr float kExp2C3 = 0x1.3babb0p-4f;   // 0.0770680308
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;              // 2 waves per SIMD
+constexpr int kWaves = 8;              // two per SIMD: one per ping-pong group
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
-constexpr int kBlockN = 64;            // keys per tile
+constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kKeyBlocks = kBlockN / 32;
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
 __device__ __forceinline__ float exp2_hw(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
@@ -90,47 +108,92 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
+// Two fp32 values -> two bf16 (round to nearest even) in one dword, low first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;   // round to nearest even
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// LDS tile layouts (bf16 elements, row-major, padded rows):
-//  K tile [kBlockN][DQK + 8]: the 16-byte pad shifts consecutive rows by 4
-//    banks, so the 16 rows one ds_read_b128 phase touches (same column chunk)
-//    land in 16 distinct 4-bank groups.
-//  V tile [kBlockN][DV + 32]: the 64-byte pad shifts consecutive rows by 16
-//    banks, so the 4 rows x 64 bytes a half-wave of ds_read_b64_tr_b16 reads
-//    cover all 64 banks once.
-template <int DQK, int DV>
-struct TileLayout {
-  static constexpr int K_PITCH = DQK + 8;
-  static constexpr int V_PITCH = DV + 32;
-  static constexpr int K_ELEMS = kBlockN * K_PITCH;
-  static constexpr int V_ELEMS = kBlockN * V_PITCH;
-  static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = kBlockN * DQK / 8;   // 16-byte chunks per K tile
-  static constexpr int V_CHUNKS = kBlockN * DV / 8;
-  static constexpr int K_LOADS = (K_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int V_LOADS = (V_CHUNKS + kThreads - 1) / kThreads;
+// LDS tile layouts.  Each 64-key tile is stored dense (row r = key k0 + r,
+// R = d/8 chunks of 16 bytes per row); the chunk of column block c of row r
+// sits at position c ^ f(r) within the row, so that
+//  * K: the 16 rows one quarter-wave ds_read_b128 phase touches (same chunk,
+//    16 consecutive rows) land in 16 distinct 4-bank groups;
+//       f_K(r) = r mod 16          when R is a multiple of 16 (d = 128)
+//       f_K(r) = (r/2) mod 8       when R = 8 or 24 (d = 64, 192: two rows
+//                                  share a 64-bank window or alternate halves)
+//  * V: the 4 rows x 4 chunks a half-wave ds_read_b64_tr_b16 touches cover 16
+//    distinct 4-bank groups;
+//       f_V(r) = 4 (r mod 4)       when R = 16
+//       f_V(r) = 4 ((r/2) mod 2)   when R = 8
+// Dense rows let each wave fill 1 KB of a tile with one buffer_load ... lds
+// (lane i writes bytes 16i..16i+15 of the 1 KB block), no VGPR staging.
+template <int D>
+struct KSwz {
+  static constexpr int R = D / 8;
+  __device__ static int f(int r) { return (R % 16 == 0) ? (r & 15) : ((r >> 1) & 7); }
+};
+template <int D>
+struct VSwz {
+  static constexpr int R = D / 8;
+  static_assert(R == 16 || R == 8, "V rows of 64 or 128 elements");
+  __device__ static int f(int r) { return (R == 16) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+template <int DQK, int DV>
+struct TileLayout {
+  static constexpr int K_ELEMS = kBlockN * DQK;          // dense K tile
+  static constexpr int V_ELEMS = kBlockN * DV;           // dense V tile
+  static constexpr int K_ISSUES = (K_ELEMS / 512) / kWaves;   // 1 KB loads per wave per K tile
+  static constexpr int V_ISSUES = (V_ELEMS / 512) / kWaves;
+  static_assert((K_ELEMS / 512) % kWaves == 0 && (V_ELEMS / 512) % kWaves == 0, "tile split");
+};
+
+// Issue one tile's buffer_load ... lds requests for this wave: request i
+// copies the 16-byte chunk at byte offset lane_off[i] + tile_off (from the
+// resource base) to bytes 16*lane .. 16*lane+15 of the 1 KB block dst[i].
+// Offsets past nbytes read as zeros.
+// The buffer resource type exists only for the device target, so the host
+// compilation pass (which only needs the kernels' launch stubs) sees an
+// empty body.
+template <int ISSUES>
+__device__ __forceinline__ void tile_load_lds(const void* base, uint32_t nbytes, const uint32_t (&lane_off)[ISSUES],
+                                              uint32_t tile_off, lds_u16_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < ISSUES; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + i * 512), 16,
+                                             lane_off[i], tile_off, 0, 0);
+#endif
+}
+
+struct Grp0 { static constexpr int value = 0; };
+struct Grp1 { static constexpr int value = 1; };
+struct NoMask { static constexpr bool value = false; };
+struct Mask { static constexpr bool value = true; };
+
 template <int DQK, int DV, bool CAUSAL, int NPOLY>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdParams p) {
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
   using Lay = TileLayout<DQK, DV>;
   constexpr int QK_STEPS = DQK / 16;             // MFMA k-steps for S^T
   constexpr int D_BLOCKS = DV / 32;              // 32-row blocks of O^T
+  constexpr int RK = DQK / 8;                    // 16-byte chunks per K row
+  constexpr int RV = DV / 8;                     // 16-byte chunks per V row
 
-  // two stages, each holding one K tile and one V tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Lay::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * Lay::K_ELEMS + 2 * Lay::V_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+  auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * Lay::K_ELEMS; };
+  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + 2 * Lay::K_ELEMS + i * Lay::V_ELEMS; };
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave / 4;      // ping-pong group
   const int lane = tid % kWave;
   const int g = lane / 32;       // lane half
-  const int lq = lane % 32;      // query column within the wave
+  const int lq = lane % 32;      // query column
 
   // ---- work decode: blockIdx = (head, sequence, query-block slot)
   const int h = blockIdx.x;
@@ -154,20 +217,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   const int H = p.H;
   const int64_t qk_row = (int64_t)H * DQK;   // elements between consecutive tokens
   const int64_t v_row = (int64_t)H * DV;
-  const uint16_t* __restrict__ kbase = p.k + (int64_t)seq0 * qk_row + (int64_t)h * DQK;
-  const uint16_t* __restrict__ vbase = p.v + (int64_t)seq0 * v_row + (int64_t)h * DV;
 
   const int qw0 = q0 + kRowsPerWave * wave;   // first query row of this wave
-  const int qrow = qw0 + lq;                  // this lane's query row (position in the sequence)
+  // last key tile with a key visible to some row of this wave
+  const int t_last = CAUSAL ? min(ntiles - 1, (qw0 + kRowsPerWave - 1) / kBlockN) : ntiles - 1;
+  const int qrow = qw0 + lq;
   const bool row_valid = qrow < L;
 
   // ---- Q^T operand, resident for the whole key loop.  Lane (g, lq) holds
   // Q[qrow][16*ks + 8*g + i], i = 0..7, for every k-step ks.
   bf16x8_t qreg[QK_STEPS];
   {
+    const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
     const int qr = min(qrow, L - 1);
     const uint16_t* qp = p.q + (int64_t)(seq0 + qr) * qk_row + (int64_t)h * DQK + 8 * g;
-    const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) {
       u32x4_t raw = *(const u32x4_t*)(qp + 16 * ks);
@@ -176,57 +239,68 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- staging registers for the next K/V tile (global -> VGPR -> LDS)
-  u32x4_t kst[Lay::K_LOADS];
-  u32x4_t vst[Lay::V_LOADS];
-
-  auto load_tile = [&](int k0) {
+  // ---- K/V tiles: HBM -> LDS with buffer_load ... lds.  The buffer range of
+  // each of K and V starts at this (sequence, head) and ends after key L-1,
+  // so keys past the sequence end read as zeros.
+  const uint32_t k_rowbytes = (uint32_t)(qk_row * 2);
+  const uint32_t v_rowbytes = (uint32_t)(v_row * 2);
+  const void* const k_head = p.k + (int64_t)seq0 * qk_row + (int64_t)h * DQK;
+  const void* const v_head = p.v + (int64_t)seq0 * v_row + (int64_t)h * DV;
+  const uint32_t k_bytes = (uint32_t)((L - 1) * (int64_t)qk_row * 2 + DQK * 2);
+  const uint32_t v_bytes = (uint32_t)((L - 1) * (int64_t)v_row * 2 + DV * 2);
+  // lane byte offsets (within a tile) of the chunks this lane loads
+  uint32_t koff[Lay::K_ISSUES], voff[Lay::V_ISSUES];
 #pragma unroll
-    for (int i = 0; i < Lay::K_LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / (DQK / 8);
-      const int col8 = c % (DQK / 8);
-      const int key = k0 + row;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (c < Lay::K_CHUNKS && key < L) val = *(const u32x4_t*)(kbase + (int64_t)key * qk_row + col8 * 8);
-      kst[i] = val;
-    }
+  for (int i = 0; i < Lay::K_ISSUES; ++i) {
+    const int slot = (wave * Lay::K_ISSUES + i) * 64 + lane;
+    const int row = slot / RK, pos = slot % RK;
+    koff[i] = (uint32_t)row * k_rowbytes + (uint32_t)(pos ^ KSwz<DQK>::f(row)) * 16u;
+  }
 #pragma unroll
-    for (int i = 0; i < Lay::V_LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / (DV / 8);
-      const int col8 = c % (DV / 8);
-      const int key = k0 + row;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (c < Lay::V_CHUNKS && key < L) val = *(const u32x4_t*)(vbase + (int64_t)key * v_row + col8 * 8);
-      vst[i] = val;
-    }
+  for (int i = 0; i < Lay::V_ISSUES; ++i) {
+    const int slot = (wave * Lay::V_ISSUES + i) * 64 + lane;
+    const int row = slot / RV, pos = slot % RV;
+    voff[i] = (uint32_t)row * v_rowbytes + (uint32_t)(pos ^ VSwz<DV>::f(row)) * 16u;
+  }
+  auto load_k = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
+    tile_load_lds<Lay::K_ISSUES>(k_head, k_bytes, koff, (uint32_t)(t * kBlockN) * k_rowbytes,
+                                 dst + wave * Lay::K_ISSUES * 512);
+  };
+  auto load_v = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
+    tile_load_lds<Lay::V_ISSUES>(v_head, v_bytes, voff, (uint32_t)(t * kBlockN) * v_rowbytes,
+                                 dst + wave * Lay::V_ISSUES * 512);
   };
 
-  auto store_tile = [&](int stage) {
-    lds_u16_t* ks_ = (lds_u16_t*)smem + stage * Lay::STAGE_ELEMS;
-    lds_u16_t* vs_ = ks_ + Lay::K_ELEMS;
+  // K rows are read in the order sigma(m) = m with bits 2 and 3 swapped: then
+  // accumulator registers 0..7 (and 8..15) of a 32-key block hold 8
+  // consecutive keys -- exactly the B-operand slots of the second product.
+  // Per k-step LDS element offsets of this lane's K chunk (row sigma(lq)).
+  int kread[QK_STEPS];
+  {
+    const int sig = (lq & ~0xC) | ((lq & 4) << 1) | ((lq & 8) >> 1);
 #pragma unroll
-    for (int i = 0; i < Lay::K_LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      if (c < Lay::K_CHUNKS) {
-        const int row = c / (DQK / 8);
-        const int col8 = c % (DQK / 8);
-        *(lds_u32x4_t*)(ks_ + row * Lay::K_PITCH + col8 * 8) = kst[i];
-      }
-    }
+    for (int ks = 0; ks < QK_STEPS; ++ks) kread[ks] = sig * DQK + (((2 * ks + g) ^ KSwz<DQK>::f(sig)) * 8);
+  }
+  // ds_read_b64_tr_b16 source addressing for the V^T operand: in each group of
+  // 16 lanes, lane s reads 4 consecutive d-values of key row s/4; the
+  // transpose hands lane i the values of 4 consecutive keys at d-column i.
+  // Rows read are 4-aligned blocks plus s/4, so f_V depends on s/4 only.
+  int vread[D_BLOCKS];
+  {
+    const int lg = lane / 16;
+    const int sl = lane % 16;
+    const int vrow = 8 * (lg / 2) + sl / 4;
 #pragma unroll
-    for (int i = 0; i < Lay::V_LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      if (c < Lay::V_CHUNKS) {
-        const int row = c / (DV / 8);
-        const int col8 = c % (DV / 8);
-        *(lds_u32x4_t*)(vs_ + row * Lay::V_PITCH + col8 * 8) = vst[i];
-      }
+    for (int db = 0; db < D_BLOCKS; ++db) {
+      const int d = db * 32 + 16 * (lg % 2) + 4 * (sl % 4);
+      vread[db] = vrow * DV + (((d / 8) ^ VSwz<DV>::f(vrow)) * 8) + (d % 8);
     }
-  };
+  }
 
-  // ---- running state: O^T accumulators, row max (log2 units), lane-partial row sum
+  // ---- per-wave state: S^T of the tile between its two phases, P^T as bf16
+  // B operands, O^T accumulators, running max (log2 units) and lane-partial sum
+  f32x16_t sacc[kKeyBlocks];
+  u32x4_t pb[kKeyBlocks][2];
   f32x16_t oacc[D_BLOCKS];
 #pragma unroll
   for (int db = 0; db < D_BLOCKS; ++db)
@@ -237,138 +311,155 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   const float c = p.c;
   const float tau = p.tau;
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
-  bool first = true;
 
-  // K rows are read in the order sigma(m) = m with bits 2 and 3 swapped: then
-  // accumulator registers 0..7 (and 8..15) of a 32-key block hold 8
-  // consecutive keys -- exactly the B-operand slots of the second product.
-  const int sig = (lq & ~0xC) | ((lq & 4) << 1) | ((lq & 8) >> 1);
-  // ds_read_b64_tr_b16 source addressing for the V^T operand: in each group of
-  // 16 lanes, lane s reads 4 consecutive d-values of key row s/4; the
-  // transpose hands lane i the values of 4 consecutive keys at d-column i.
-  const int grp = lane / 16;
-  const int sl = lane % 16;
-  const int v_key_off = 8 * (grp / 2) + sl / 4;
-  const int v_col_off = 16 * (grp % 2) + 4 * (sl % 4);
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * kBlockN;
-    const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(k0 + kBlockN);
-
-    if (!CAUSAL || k0 <= qw0 + kRowsPerWave - 1) {   // else: every key is above this wave's rows
-      ++n_tiles;
-      const lds_u16_t* ks_ = (const lds_u16_t*)smem + stage * Lay::STAGE_ELEMS;
-      const lds_u16_t* vs_ = ks_ + Lay::K_ELEMS;
-
-      // ---- S^T = K Q^T
-      f32x16_t sacc[kKeyBlocks];
+  // S^T tile = K_t Q^T
+  auto gemm_qk = [&] __device__ (const lds_u16_t* kt) __attribute__((always_inline)) {
+    const f32x16_t zero = {};
 #pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb) {
-          const bf16x8_t a = *(const lds_bf16x8_t*)(ks_ + (kb * 32 + sig) * Lay::K_PITCH + 16 * ks + 8 * g);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
-        }
-      }
-
-      // ---- mask (only tiles that reach past the sequence end or this wave's diagonal)
-      const bool need_mask = (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-            if (key > lim) sacc[kb][r] = -__builtin_inff();
-          }
-      }
-
-      // ---- row max of this tile (raw logits; c > 0 so max commutes with scaling)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sacc[kb][r]);
-      mx = max_with_partner(mx);
-      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-
-      // ---- conditional rescale
-      if (first) {
-        m_run = m_tile;   // O and l are still zero: nothing to rescale
-        first = false;
-      } else {
-        bool need;
-        float m_new;
-        if (tau < 0.0f) {                 // classic online softmax: always rescale
-          m_new = __builtin_fmaxf(m_run, m_tile);
-          need = true;
-        } else {
-          need = m_tile > m_run + tau;
-          m_new = need ? m_tile : m_run;
-        }
-        if (row_valid && g == 0) {
-          n_considered += 1;
-          n_taken += need ? 1u : 0u;
-        }
-        if (tau < 0.0f || __builtin_amdgcn_ballot_w64(need) != 0) {
-          const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
-#pragma unroll
-          for (int db = 0; db < D_BLOCKS; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-          l_part *= alpha;
-          m_run = m_new;
-        }
-      }
-
-      // ---- P = exp2(c*s - m), row sum, bf16 B operand
-      u32x4_t pb[kKeyBlocks][2];
-      const float neg_m = -m_run;
+    for (int ks = 0; ks < QK_STEPS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
-          pv[r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
-          l_part += pv[r];
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pb[kb][hh][j] = pack_bf16x2(pv[8 * hh + 2 * j], pv[8 * hh + 2 * j + 1]);
+        const bf16x8_t a = *(const lds_bf16x8_t*)(kt + kread[ks] + kb * 32 * DQK);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
       }
+    }
+  };
+  // O^T += V_t^T P_t^T
+  auto gemm_pv = [&] __device__ (const lds_u16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb[kb][hh]);
+#pragma unroll
+        for (int db = 0; db < D_BLOCKS; ++db) {
+          const lds_u16_t* vr = vt + vread[db] + (kb * 32 + 16 * hh) * DV;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr + 4 * DV));
+          const i16x4_t both[2] = {lo, hi};
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[db], 0, 0, 0);
+        }
+      }
+  };
 
-      // ---- O^T += V^T P^T  (V^T operand by transposing LDS reads)
+  // Softmax of tile t (in sacc): masks, row max, conditional rescale of O and
+  // l, P = exp2(c s - m) as bf16 B operands, and the row sums.
+  auto softmax = [&] __device__ (auto mask_tag, int t) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = t * kBlockN;
+    if (MASK) {
+      const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb[kb][hh]);
-          const lds_u16_t* vrow = vs_ + (kb * 32 + 16 * hh + v_key_off) * Lay::V_PITCH + v_col_off;
-#pragma unroll
-          for (int db = 0; db < D_BLOCKS; ++db) {
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + db * 32));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vrow + 4 * Lay::V_PITCH + db * 32));
-            const i16x4_t both[2] = {lo, hi};
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[db], 0, 0, 0);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+          if (key > lim) sacc[kb][r] = -__builtin_inff();
         }
     }
+    // row max of this tile (raw logits; c > 0 so max commutes with scaling)
+    float mx0 = sacc[0][0], mx1 = sacc[0][1];
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
+        mx0 = __builtin_fmaxf(mx0, sacc[kb][r]);
+        mx1 = __builtin_fmaxf(mx1, sacc[kb][r + 1]);
+      }
+    const float mx = max_with_partner(__builtin_fmaxf(mx0, mx1));
+    const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
+    if (t == 0) {
+      m_run = m_tile;   // O and l are still zero: nothing to rescale
+    } else {
+      bool need;
+      float m_new;
+      if (tau < 0.0f) {                 // classic online softmax: always rescale
+        m_new = __builtin_fmaxf(m_run, m_tile);
+        need = true;
+      } else {
+        need = m_tile > m_run + tau;
+        m_new = need ? m_tile : m_run;
+      }
+      if (row_valid && g == 0) {
+        n_considered += 1;
+        n_taken += need ? 1u : 0u;
+      }
+      if (tau < 0.0f || __builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < D_BLOCKS; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_part *= alpha;
+        m_run = m_new;
+      }
+    }
+    const float neg_m = -m_run;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
+        pv[r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
+        acc[r % 4] += pv[r];
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pb[kb][hh][j] = pack_bf16x2(pv[8 * hh + 2 * j], pv[8 * hh + 2 * j + 1]);
+    }
+    l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
 
-    if (t + 1 < ntiles) store_tile(stage ^ 1);
-    __syncthreads();
-  }
+  // Does the softmax of tile t need masking for this wave?
+  auto needs_mask = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int k0 = t * kBlockN;
+    return (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
+  };
+
+  // ---- phases.  Group grp runs the matrix phase of tile j at phase 2j+grp
+  // (O += V[j-1] P[j-1], then S[j] = K[j] Q^T) and the softmax of tile j at
+  // phase 2j+1+grp.  K[j] and V[j-1] are read in phases 2j and 2j+1; the
+  // loads of K[j+1] and V[j] are issued at the start of phase 2j into the
+  // buffers last read in phases 2j-2 and 2j-1.
+  auto matrix_phase = [&] __device__ (int j) __attribute__((always_inline)) {
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    if (j >= 1 && j - 1 <= t_last) gemm_pv(vbuf((j - 1) & 1));
+    if (j < ntiles && j <= t_last) {
+      gemm_qk(kbuf(j & 1));
+      ++n_tiles;
+    }
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
+    if (j >= 0 && j < ntiles && j <= t_last) {
+      if (needs_mask(j)) softmax(Mask{}, j);
+      else softmax(NoMask{}, j);
+    }
+  };
+  // Each group's loop is straight-line per iteration (two phases, two
+  // barriers); group 1 runs the softmax of the previous tile first.  Every
+  // wave runs ntiles + 1 iterations, so the barrier counts agree.
+  auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp_tag)::value;
+    for (int j = 0; j <= ntiles; ++j) {
+      if (j + 1 < ntiles) load_k(j + 1, kbuf((j + 1) & 1));
+      if (j < ntiles) load_v(j, vbuf(j & 1));
+      if (G == 0) matrix_phase(j);
+      else softmax_phase(j - 1);
+      __syncthreads();
+      if (G == 0) softmax_phase(j);
+      else matrix_phase(j);
+      __syncthreads();
+    }
+  };
+  load_k(0, kbuf(0));
+  __syncthreads();
+  if (grp == 0) run(Grp0{});
+  else run(Grp1{});
 
   // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2
   const float l_tot = sum_with_partner(l_part);
@@ -378,11 +469,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int db = 0; db < D_BLOCKS; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int jj = 0; jj < 4; ++jj) {
         u32x2_t w;
-        w.x = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *(u32x2_t*)(op + db * 32 + 8 * j + 4 * g) = w;
+        w.x = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+        w.y = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+        *(u32x2_t*)(op + db * 32 + 8 * jj + 4 * g) = w;
       }
     if (g == 0) {
       p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
