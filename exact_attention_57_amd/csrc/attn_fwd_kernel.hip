@@ -108,6 +108,15 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
+// x *= a, in the register that holds x.  The O accumulators are rescaled
+// only on the rare tiles whose row max grew; writing the product back into
+// the same register keeps the allocator from copying all of O on the common
+// path that skips the multiply.  (Every MFMA that wrote x completed before
+// the barrier that precedes any rescale.)
+__device__ __forceinline__ void scale_in_place(float& x, float a) {
+  asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(a));
+}
+
 // Two fp32 values -> two bf16 (round to nearest even) in one dword, low first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
@@ -343,12 +352,24 @@ void attn_fwd_kernel(FwdParams p) {
       }
   };
 
+  // Does the softmax of tile t need masking for this wave?
+  auto needs_mask = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int k0 = t * kBlockN;
+    return (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
+  };
+
+  // ---- phases.  Group grp runs the matrix phase of tile j at phase 2j+grp
+  // (O += V[j-1] P[j-1], then S[j] = K[j] Q^T) and the softmax of tile j at
+  // phase 2j+1+grp.  K[j] and V[j-1] are read in phases 2j and 2j+1; the
+  // loads of K[j+1] and V[j] are issued at the start of phase 2j into the
+  // buffers last read in phases 2j-2 and 2j-1.
   // Softmax of tile t (in sacc): masks, row max, conditional rescale of O and
   // l, P = exp2(c s - m) as bf16 B operands, and the row sums.
-  auto softmax = [&] __device__ (auto mask_tag, int t) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto softmax = [&] __device__ (int t) __attribute__((always_inline)) {
     const int k0 = t * kBlockN;
-    if (MASK) {
+    // the mask only touches S; keeping it a separate branch leaves one path
+    // through the O rescale below
+    if (needs_mask(t)) {
       const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
@@ -390,7 +411,11 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int db = 0; db < D_BLOCKS; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) {
+            float x = oacc[db][r];
+            scale_in_place(x, alpha);
+            oacc[db][r] = x;
+          }
         l_part *= alpha;
         m_run = m_new;
       }
@@ -414,17 +439,6 @@ void attn_fwd_kernel(FwdParams p) {
     l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
 
-  // Does the softmax of tile t need masking for this wave?
-  auto needs_mask = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * kBlockN;
-    return (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
-  };
-
-  // ---- phases.  Group grp runs the matrix phase of tile j at phase 2j+grp
-  // (O += V[j-1] P[j-1], then S[j] = K[j] Q^T) and the softmax of tile j at
-  // phase 2j+1+grp.  K[j] and V[j-1] are read in phases 2j and 2j+1; the
-  // loads of K[j+1] and V[j] are issued at the start of phase 2j into the
-  // buffers last read in phases 2j-2 and 2j-1.
   auto matrix_phase = [&] __device__ (int j) __attribute__((always_inline)) {
     if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     if (j >= 1 && j - 1 <= t_last) gemm_pv(vbuf((j - 1) & 1));
@@ -436,8 +450,7 @@ void attn_fwd_kernel(FwdParams p) {
   };
   auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
     if (j >= 0 && j < ntiles && j <= t_last) {
-      if (needs_mask(j)) softmax(Mask{}, j);
-      else softmax(NoMask{}, j);
+      softmax(j);
     }
   };
   // Each group's loop is straight-line per iteration (two phases, two
