@@ -127,8 +127,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB 5 times (for scaling "
-                         "FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
+                    help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
+                         "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -146,7 +146,7 @@ def main():
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)     # one elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": 5}), flush=True)

@@ -161,19 +161,56 @@ struct TileLayout {
 // Issue one tile's buffer_load ... lds requests for this wave: request i
 // copies the 16-byte chunk at byte offset lane_off[i] + tile_off (from the
 // resource base) to bytes 16*lane .. 16*lane+15 of the 1 KB block dst[i].
-// Offsets past nbytes read as zeros.
-// The buffer resource type exists only for the device target, so the host
-// compilation pass (which only needs the kernels' launch stubs) sees an
-// empty body.
+// Offsets past the resource's byte count read as zeros.
+//
+// The requests are written as inline assembly so that the compiler does not
+// track them: it cannot tell which LDS buffer a DMA writes, and would make
+// every later LDS read wait for all DMAs in flight.  Completion is instead
+// awaited explicitly (phase_barrier<true> below) one phase before the first
+// read of the tile.  The host compilation pass only needs the kernels' launch
+// stubs and sees an empty body.
 template <int ISSUES>
-__device__ __forceinline__ void tile_load_lds(const void* base, uint32_t nbytes, const uint32_t (&lane_off)[ISSUES],
+__device__ __forceinline__ void tile_load_lds(const u32x4_t& rsrc, const uint32_t (&lane_off)[ISSUES],
                                               uint32_t tile_off, lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)dst;
 #pragma unroll
-  for (int i = 0; i < ISSUES; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + i * 512), 16,
-                                             lane_off[i], tile_off, 0, 0);
+  for (int i = 0; i < ISSUES; ++i) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + i * 1024u);
+    // s_nop: one wait state between the M0 write and its use by an LDS DMA
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "{m0}"(m0), "v"(lane_off[i]), "s"(rsrc), "s"(tile_off)
+                 : "memory");
+  }
+#endif
+}
+
+// Buffer resource for a byte range starting at base: raw (unswizzled)
+// addressing, no stride, num_records = nbytes, so that reads at or past
+// nbytes return zeros.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(nbytes);
+  r.w = 0x00020000u;
+  return r;
+}
+
+// Workgroup barrier for the phase schedule.  Every wave first waits for its
+// own LDS reads (the buffer may be refilled after the barrier) and, with
+// WAIT_DMA, for its tile DMAs, so that after the barrier every wave sees the
+// complete tiles.  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+template <bool WAIT_DMA>
+__device__ __forceinline__ void phase_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (WAIT_DMA)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #endif
 }
 
@@ -271,12 +308,14 @@ void attn_fwd_kernel(FwdParams p) {
     const int row = slot / RV, pos = slot % RV;
     voff[i] = (uint32_t)row * v_rowbytes + (uint32_t)(pos ^ VSwz<DV>::f(row)) * 16u;
   }
+  const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
+  const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
   auto load_k = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
-    tile_load_lds<Lay::K_ISSUES>(k_head, k_bytes, koff, (uint32_t)(t * kBlockN) * k_rowbytes,
+    tile_load_lds<Lay::K_ISSUES>(k_rsrc, koff, (uint32_t)(t * kBlockN) * k_rowbytes,
                                  dst + wave * Lay::K_ISSUES * 512);
   };
   auto load_v = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
-    tile_load_lds<Lay::V_ISSUES>(v_head, v_bytes, voff, (uint32_t)(t * kBlockN) * v_rowbytes,
+    tile_load_lds<Lay::V_ISSUES>(v_rsrc, voff, (uint32_t)(t * kBlockN) * v_rowbytes,
                                  dst + wave * Lay::V_ISSUES * 512);
   };
 
@@ -463,14 +502,14 @@ void attn_fwd_kernel(FwdParams p) {
       if (j < ntiles) load_v(j, vbuf(j & 1));
       if (G == 0) matrix_phase(j);
       else softmax_phase(j - 1);
-      __syncthreads();
+      phase_barrier<false>();
       if (G == 0) softmax_phase(j);
       else matrix_phase(j);
-      __syncthreads();
+      phase_barrier<true>();    // K[j+1] and V[j] complete: first read next phase
     }
   };
   load_k(0, kbuf(0));
-  __syncthreads();
+  phase_barrier<true>();
   if (grp == 0) run(Grp0{});
   else run(Grp1{});
 
