@@ -48,6 +48,9 @@
 
 #include "attn_fwd_kernel.h"
 
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 4  // matrix-phase LDS operands read ahead of their MFMA
+#endif
 #ifndef ATTN_SETPRIO
 #define ATTN_SETPRIO 1  // raise the issue priority of the wave in its matrix phase
 #endif
@@ -214,6 +217,28 @@ __device__ __forceinline__ void phase_barrier() {
 #endif
 }
 
+// Order of the matrix phase's instructions for the scheduler: the LDS reads
+// of the first kPrefetch slots, then per slot s the reads of slot
+// s + kPrefetch (two transposing reads for an output-product slot, one for a
+// score-product slot) followed by the MFMA of slot s.
+constexpr int kPrefetch = ATTN_PREFETCH;
+template <int S, int NS, int NPV>
+__device__ __forceinline__ void pin_matrix_schedule() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  if constexpr (S == 0) {
+    constexpr int n0 = (kPrefetch < NS ? kPrefetch : NS);
+    constexpr int reads = 2 * (n0 < NPV ? n0 : NPV) + (n0 > NPV ? n0 - NPV : 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, reads, 0);
+  }
+  if constexpr (S < NS) {
+    if constexpr (S + kPrefetch < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, (S + kPrefetch < NPV) ? 2 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    pin_matrix_schedule<S + 1, NS, NPV>();
+  }
+}
+
+struct True { static constexpr bool value = true; };
+struct False { static constexpr bool value = false; };
 struct Grp0 { static constexpr int value = 0; };
 struct Grp1 { static constexpr int value = 1; };
 struct NoMask { static constexpr bool value = false; };
@@ -349,6 +374,10 @@ void attn_fwd_kernel(FwdParams p) {
   // B operands, O^T accumulators, running max (log2 units) and lane-partial sum
   f32x16_t sacc[kKeyBlocks];
   u32x4_t pb[kKeyBlocks][2];
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) pb[kb][hh] = u32x4_t{0u, 0u, 0u, 0u};
   f32x16_t oacc[D_BLOCKS];
 #pragma unroll
   for (int db = 0; db < D_BLOCKS; ++db)
@@ -360,35 +389,51 @@ void attn_fwd_kernel(FwdParams p) {
   const float tau = p.tau;
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
 
-  // S^T tile = K_t Q^T
-  auto gemm_qk = [&] __device__ (const lds_u16_t* kt) __attribute__((always_inline)) {
+  // One matrix phase as a single stream of MFMA slots: first the output
+  // product O^T += V_t^T P_t^T (slots (kb, hh, db), db fastest, so neighbours
+  // accumulate into different blocks), then the score product S^T = K_t Q^T
+  // (slots (ks, kb)).  The LDS operand of slot s + kPrefetch is read before
+  // the MFMA of slot s, and pin_matrix_schedule fixes that order, so each read
+  // has several MFMAs (32 cycles each) to return.
+  auto matrix = [&] __device__ (auto pv_tag, auto qk_tag, const lds_u16_t* vt, const lds_u16_t* kt)
+      __attribute__((always_inline)) {
+    constexpr bool DO_PV = decltype(pv_tag)::value;
+    constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr int NPV = DO_PV ? kKeyBlocks * 2 * D_BLOCKS : 0;
+    constexpr int NQK = DO_QK ? QK_STEPS * kKeyBlocks : 0;
+    constexpr int NS = NPV + NQK;
+    // A operand of slot s: for the output product two transposing reads give
+    // V^T rows db*32.. at keys kb*32 + 16hh + (0..7); for the score product
+    // one 16-byte read gives K row sigma(lq) of key block kb at k-step ks.
+    auto read_op = [&] __device__ (int s) __attribute__((always_inline)) -> bf16x8_t {
+      if (s < NPV) {
+        const int kb = s / (2 * D_BLOCKS), hh = (s / D_BLOCKS) % 2, db = s % D_BLOCKS;
+        const lds_u16_t* vr = vt + vread[db] + (kb * 32 + 16 * hh) * DV;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr + 4 * DV));
+        const i16x4_t both[2] = {lo, hi};
+        return __builtin_bit_cast(bf16x8_t, both);
+      }
+      const int q = s - NPV, ks = q / kKeyBlocks, kb = q % kKeyBlocks;
+      return *(const lds_bf16x8_t*)(kt + kread[ks] + kb * 32 * DQK);
+    };
+    bf16x8_t op[NS];
+#pragma unroll
+    for (int s = 0; s < kPrefetch && s < NS; ++s) op[s] = read_op(s);
     const f32x16_t zero = {};
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb) {
-        const bf16x8_t a = *(const lds_bf16x8_t*)(kt + kread[ks] + kb * 32 * DQK);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
+    for (int s = 0; s < NS; ++s) {
+      if (s + kPrefetch < NS) op[s + kPrefetch] = read_op(s + kPrefetch);
+      if (s < NPV) {
+        const int kb = s / (2 * D_BLOCKS), hh = (s / D_BLOCKS) % 2, db = s % D_BLOCKS;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], __builtin_bit_cast(bf16x8_t, pb[kb][hh]),
+                                                           oacc[db], 0, 0, 0);
+      } else {
+        const int q = s - NPV, ks = q / kKeyBlocks, kb = q % kKeyBlocks;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
       }
     }
-  };
-  // O^T += V_t^T P_t^T
-  auto gemm_pv = [&] __device__ (const lds_u16_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb[kb][hh]);
-#pragma unroll
-        for (int db = 0; db < D_BLOCKS; ++db) {
-          const lds_u16_t* vr = vt + vread[db] + (kb * 32 + 16 * hh) * DV;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr + 4 * DV));
-          const i16x4_t both[2] = {lo, hi};
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[db], 0, 0, 0);
-        }
-      }
+    pin_matrix_schedule<0, NS, NPV>();
   };
 
   // Does the softmax of tile t need masking for this wave?
@@ -441,7 +486,7 @@ void attn_fwd_kernel(FwdParams p) {
         need = m_tile > m_run + tau;
         m_new = need ? m_tile : m_run;
       }
-      if (row_valid && g == 0) {
+      if (row_valid && g == 0 && t <= t_last) {
         n_considered += 1;
         n_taken += need ? 1u : 0u;
       }
@@ -478,19 +523,20 @@ void attn_fwd_kernel(FwdParams p) {
     l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
 
+  // Every iteration runs the same matrix code, so the O accumulators keep
+  // one register assignment: at j = 0 the output product multiplies zero P
+  // with the zero-filled V buffer 1, and at j = ntiles the score product of a
+  // stale K buffer is computed and dropped.  Causal tiles past a wave's
+  // diagonal go through the softmax fully masked (P = 0, no rescale), which
+  // leaves O, l and m exactly as skipping them would.
   auto matrix_phase = [&] __device__ (int j) __attribute__((always_inline)) {
     if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    if (j >= 1 && j - 1 <= t_last) gemm_pv(vbuf((j - 1) & 1));
-    if (j < ntiles && j <= t_last) {
-      gemm_qk(kbuf(j & 1));
-      ++n_tiles;
-    }
+    matrix(True{}, True{}, vbuf((j - 1) & 1), kbuf(j & 1));
     if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    n_tiles += (j < ntiles && j <= t_last) ? 1u : 0u;
   };
   auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
-    if (j >= 0 && j < ntiles && j <= t_last) {
-      softmax(j);
-    }
+    if (j >= 0 && j < ntiles) softmax(j);
   };
   // Each group's loop is straight-line per iteration (two phases, two
   // barriers); group 1 runs the softmax of the previous tile first.  Every
@@ -508,6 +554,8 @@ void attn_fwd_kernel(FwdParams p) {
       phase_barrier<true>();    // K[j+1] and V[j] complete: first read next phase
     }
   };
+  // V buffer 1 is read (times P = 0) before its first fill
+  for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
   load_k(0, kbuf(0));
   phase_barrier<true>();
   if (grp == 0) run(Grp0{});
