@@ -152,40 +152,40 @@ struct VSwz {
   __device__ static int f(int r) { return (R == 16) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// Tiles are filled by the four group-0 waves, during their matrix phases.
+constexpr int kLoaders = kWaves / 2;
+constexpr int kBufs = 3;                 // K and V tile buffers in LDS
+
 template <int DQK, int DV>
 struct TileLayout {
   static constexpr int K_ELEMS = kBlockN * DQK;          // dense K tile
   static constexpr int V_ELEMS = kBlockN * DV;           // dense V tile
-  static constexpr int K_ISSUES = (K_ELEMS / 512) / kWaves;   // 1 KB loads per wave per K tile
-  static constexpr int V_ISSUES = (V_ELEMS / 512) / kWaves;
-  static_assert((K_ELEMS / 512) % kWaves == 0 && (V_ELEMS / 512) % kWaves == 0, "tile split");
+  static constexpr int K_ISSUES = (K_ELEMS / 512) / kLoaders;   // 1 KB DMAs per loader wave per K tile
+  static constexpr int V_ISSUES = (V_ELEMS / 512) / kLoaders;
+  static constexpr int ISSUES = K_ISSUES + V_ISSUES;
+  static_assert((K_ELEMS / 512) % kLoaders == 0 && (V_ELEMS / 512) % kLoaders == 0, "tile split");
 };
 
-// Issue one tile's buffer_load ... lds requests for this wave: request i
-// copies the 16-byte chunk at byte offset lane_off[i] + tile_off (from the
-// resource base) to bytes 16*lane .. 16*lane+15 of the 1 KB block dst[i].
-// Offsets past the resource's byte count read as zeros.
+// One buffer_load_dwordx4 ... lds request: copies, for every lane, the
+// 16-byte chunk at byte offset lane_off + tile_off (from the resource base) to
+// bytes 16*lane .. 16*lane+15 of the 1 KB LDS block at dst.  Offsets past the
+// resource's byte count read as zeros.
 //
-// The requests are written as inline assembly so that the compiler does not
-// track them: it cannot tell which LDS buffer a DMA writes, and would make
-// every later LDS read wait for all DMAs in flight.  Completion is instead
-// awaited explicitly (phase_barrier<true> below) one phase before the first
-// read of the tile.  The host compilation pass only needs the kernels' launch
-// stubs and sees an empty body.
-template <int ISSUES>
-__device__ __forceinline__ void tile_load_lds(const u32x4_t& rsrc, const uint32_t (&lane_off)[ISSUES],
-                                              uint32_t tile_off, lds_u16_t* dst) {
+// The request is inline assembly so that the compiler does not track it: it
+// cannot tell which LDS buffer a DMA writes, and would make every later LDS
+// read of the wave wait for all DMAs in flight.  Completion is awaited
+// explicitly (dma_wait_barrier) before the barrier that precedes the tile's
+// first read.  The host compilation pass only needs the kernels' launch stubs
+// and sees an empty body.
+__device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off, uint32_t tile_off,
+                                          lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t lds_base = (uint32_t)(uintptr_t)dst;
-#pragma unroll
-  for (int i = 0; i < ISSUES; ++i) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + i * 1024u);
-    // s_nop: one wait state between the M0 write and its use by an LDS DMA
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "{m0}"(m0), "v"(lane_off[i]), "s"(rsrc), "s"(tile_off)
-                 : "memory");
-  }
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  // s_nop: one wait state between the M0 write and its use by an LDS DMA
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "{m0}"(m0), "v"(lane_off), "s"(rsrc), "s"(tile_off)
+               : "memory");
 #endif
 }
 
@@ -202,38 +202,44 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t nbytes) 
   return r;
 }
 
-// Workgroup barrier for the phase schedule.  Every wave first waits for its
-// own LDS reads (the buffer may be refilled after the barrier) and, with
-// WAIT_DMA, for its tile DMAs, so that after the barrier every wave sees the
-// complete tiles.  The memory clobber keeps the compiler from moving LDS
-// accesses across it.
-template <bool WAIT_DMA>
-__device__ __forceinline__ void phase_barrier() {
+// Workgroup barriers of the phase schedule.  The memory clobber keeps the
+// compiler from moving LDS accesses across them.  No LDS wait is needed
+// before a barrier: every LDS read is either consumed by an MFMA of the same
+// phase (so it has returned) or reads a buffer that is not refilled for
+// another iteration.
+__device__ __forceinline__ void barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
-  if (WAIT_DMA)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+// Wait until at most N of this wave's DMAs are in flight, then barrier: the
+// older DMAs have landed in LDS and, once every loader has waited, are
+// visible to all waves.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+#endif
+}
+__device__ __forceinline__ void dma_wait_all() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #endif
 }
 
-// Order of the matrix phase's instructions for the scheduler: the LDS reads
-// of the first kPrefetch slots, then per slot s the reads of slot
-// s + kPrefetch (two transposing reads for an output-product slot, one for a
-// score-product slot) followed by the MFMA of slot s.
+// Order of the matrix phase's instructions for the scheduler: per slot s the
+// LDS reads of slot s + kPrefetch (one for a score-product slot, two
+// transposing reads for an output-product slot) followed by the MFMA of
+// slot s.  The reads of the first kPrefetch slots were issued at the end of
+// the wave's previous phase.
 constexpr int kPrefetch = ATTN_PREFETCH;
-template <int S, int NS, int NPV>
+template <int S, int NS, int NQK>
 __device__ __forceinline__ void pin_matrix_schedule() {
   constexpr int kDsRead = 0x100, kMfma = 0x008;
-  if constexpr (S == 0) {
-    constexpr int n0 = (kPrefetch < NS ? kPrefetch : NS);
-    constexpr int reads = 2 * (n0 < NPV ? n0 : NPV) + (n0 > NPV ? n0 - NPV : 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, reads, 0);
-  }
   if constexpr (S < NS) {
-    if constexpr (S + kPrefetch < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, (S + kPrefetch < NPV) ? 2 : 1, 0);
+    if constexpr (S + kPrefetch < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, (S + kPrefetch < NQK) ? 1 : 2, 0);
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    pin_matrix_schedule<S + 1, NS, NPV>();
+    pin_matrix_schedule<S + 1, NS, NQK>();
   }
 }
 
@@ -241,8 +247,6 @@ struct True { static constexpr bool value = true; };
 struct False { static constexpr bool value = false; };
 struct Grp0 { static constexpr int value = 0; };
 struct Grp1 { static constexpr int value = 1; };
-struct NoMask { static constexpr bool value = false; };
-struct Mask { static constexpr bool value = true; };
 
 template <int DQK, int DV, bool CAUSAL, int NPOLY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -254,10 +258,12 @@ void attn_fwd_kernel(FwdParams p) {
   constexpr int RK = DQK / 8;                    // 16-byte chunks per K row
   constexpr int RV = DV / 8;                     // 16-byte chunks per V row
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * Lay::K_ELEMS + 2 * Lay::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kBufs * Lay::K_ELEMS + kBufs * Lay::V_ELEMS];
   lds_u16_t* const lds = (lds_u16_t*)smem;
   auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * Lay::K_ELEMS; };
-  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + 2 * Lay::K_ELEMS + i * Lay::V_ELEMS; };
+  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) {
+    return lds + kBufs * Lay::K_ELEMS + i * Lay::V_ELEMS;
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -319,29 +325,32 @@ void attn_fwd_kernel(FwdParams p) {
   const void* const v_head = p.v + (int64_t)seq0 * v_row + (int64_t)h * DV;
   const uint32_t k_bytes = (uint32_t)((L - 1) * (int64_t)qk_row * 2 + DQK * 2);
   const uint32_t v_bytes = (uint32_t)((L - 1) * (int64_t)v_row * 2 + DV * 2);
-  // lane byte offsets (within a tile) of the chunks this lane loads
+  // lane byte offsets (within a tile) of the chunks this lane loads when its
+  // wave is loader lw (group 1 computes them but issues no DMA)
+  const int lw = wave % kLoaders;
   uint32_t koff[Lay::K_ISSUES], voff[Lay::V_ISSUES];
 #pragma unroll
   for (int i = 0; i < Lay::K_ISSUES; ++i) {
-    const int slot = (wave * Lay::K_ISSUES + i) * 64 + lane;
+    const int slot = (lw * Lay::K_ISSUES + i) * 64 + lane;
     const int row = slot / RK, pos = slot % RK;
     koff[i] = (uint32_t)row * k_rowbytes + (uint32_t)(pos ^ KSwz<DQK>::f(row)) * 16u;
   }
 #pragma unroll
   for (int i = 0; i < Lay::V_ISSUES; ++i) {
-    const int slot = (wave * Lay::V_ISSUES + i) * 64 + lane;
+    const int slot = (lw * Lay::V_ISSUES + i) * 64 + lane;
     const int row = slot / RV, pos = slot % RV;
     voff[i] = (uint32_t)row * v_rowbytes + (uint32_t)(pos ^ VSwz<DV>::f(row)) * 16u;
   }
   const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
   const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
-  auto load_k = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
-    tile_load_lds<Lay::K_ISSUES>(k_rsrc, koff, (uint32_t)(t * kBlockN) * k_rowbytes,
-                                 dst + wave * Lay::K_ISSUES * 512);
-  };
-  auto load_v = [&] __device__ (int t, lds_u16_t* dst) __attribute__((always_inline)) {
-    tile_load_lds<Lay::V_ISSUES>(v_rsrc, voff, (uint32_t)(t * kBlockN) * v_rowbytes,
-                                 dst + wave * Lay::V_ISSUES * 512);
+  // DMA d (0 <= d < ISSUES) of this loader's share of K tile tk then V tile tv
+  auto dma = [&] __device__ (int d, int tk, int tv, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+    if (d < Lay::K_ISSUES) {
+      dma_chunk(k_rsrc, koff[d], (uint32_t)(tk * kBlockN) * k_rowbytes, kdst + (lw * Lay::K_ISSUES + d) * 512);
+    } else {
+      const int e = d - Lay::K_ISSUES;
+      dma_chunk(v_rsrc, voff[e], (uint32_t)(tv * kBlockN) * v_rowbytes, vdst + (lw * Lay::V_ISSUES + e) * 512);
+    }
   };
 
   // K rows are read in the order sigma(m) = m with bits 2 and 3 swapped: then
@@ -370,14 +379,18 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- per-wave state: S^T of the tile between its two phases, P^T as bf16
-  // B operands, O^T accumulators, running max (log2 units) and lane-partial sum
+  // ---- per-wave state: S^T of the tile between its two phases, its raw row
+  // max, P^T in fp32 from the softmax until the next matrix phase and as bf16
+  // B operands, O^T accumulators, running max (log2 units) and lane-partial
+  // row sum
   f32x16_t sacc[kKeyBlocks];
-  u32x4_t pb[kKeyBlocks][2];
+  f32x16_t pf[kKeyBlocks];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) pb[kb][hh] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 16; ++r) pf[kb][r] = 0.0f;
+  float mx_raw = -__builtin_inff();
+  u32x4_t pb[kKeyBlocks][2];
   f32x16_t oacc[D_BLOCKS];
 #pragma unroll
   for (int db = 0; db < D_BLOCKS; ++db)
@@ -389,51 +402,105 @@ void attn_fwd_kernel(FwdParams p) {
   const float tau = p.tau;
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
 
-  // One matrix phase as a single stream of MFMA slots: first the output
-  // product O^T += V_t^T P_t^T (slots (kb, hh, db), db fastest, so neighbours
-  // accumulate into different blocks), then the score product S^T = K_t Q^T
-  // (slots (ks, kb)).  The LDS operand of slot s + kPrefetch is read before
-  // the MFMA of slot s, and pin_matrix_schedule fixes that order, so each read
-  // has several MFMAs (32 cycles each) to return.
-  auto matrix = [&] __device__ (auto pv_tag, auto qk_tag, const lds_u16_t* vt, const lds_u16_t* kt)
-      __attribute__((always_inline)) {
-    constexpr bool DO_PV = decltype(pv_tag)::value;
-    constexpr bool DO_QK = decltype(qk_tag)::value;
-    constexpr int NPV = DO_PV ? kKeyBlocks * 2 * D_BLOCKS : 0;
-    constexpr int NQK = DO_QK ? QK_STEPS * kKeyBlocks : 0;
-    constexpr int NS = NPV + NQK;
-    // A operand of slot s: for the output product two transposing reads give
-    // V^T rows db*32.. at keys kb*32 + 16hh + (0..7); for the score product
-    // one 16-byte read gives K row sigma(lq) of key block kb at k-step ks.
-    auto read_op = [&] __device__ (int s) __attribute__((always_inline)) -> bf16x8_t {
-      if (s < NPV) {
-        const int kb = s / (2 * D_BLOCKS), hh = (s / D_BLOCKS) % 2, db = s % D_BLOCKS;
-        const lds_u16_t* vr = vt + vread[db] + (kb * 32 + 16 * hh) * DV;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr + 4 * DV));
-        const i16x4_t both[2] = {lo, hi};
-        return __builtin_bit_cast(bf16x8_t, both);
+  // Row max of S^T over the tile: lane-local over its 32 keys, then with the
+  // partner lane holding the other half of the row.
+  auto row_max = [&] __device__ () __attribute__((always_inline)) -> float {
+    float mx0 = sacc[0][0], mx1 = sacc[0][1];
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
+        mx0 = __builtin_fmaxf(mx0, sacc[kb][r]);
+        mx1 = __builtin_fmaxf(mx1, sacc[kb][r + 1]);
       }
-      const int q = s - NPV, ks = q / kKeyBlocks, kb = q % kKeyBlocks;
+    return max_with_partner(__builtin_fmaxf(mx0, mx1));
+  };
+  // One matrix phase as a single stream of MFMA slots: first the score
+  // product S^T = K_t Q^T (slots (ks, kb)), then the output product
+  // O^T += V_{t-1}^T P_{t-1}^T (slots (kb, hh, db), db fastest, so neighbours
+  // accumulate into different blocks).  Alongside the MFMAs the wave rounds
+  // P_{t-1} to bf16 and adds it to the row sum, then takes the row max of
+  // S_t: VALU work that issues while the matrix core is busy, taken off the
+  // softmax phase of the other wave on the SIMD.  The LDS operand of slot s + kPrefetch is read before
+  // the MFMA of slot s, and pin_matrix_schedule fixes that order, so each read
+  // has several MFMAs (32 cycles each) to return; the operands of the first
+  // kPrefetch slots are read (prefetch) at the end of the wave's previous
+  // phase, so the stream starts without waiting for LDS.
+  constexpr int NPV = kKeyBlocks * 2 * D_BLOCKS;
+  constexpr int NQK = QK_STEPS * kKeyBlocks;
+  constexpr int NS = NPV + NQK;
+  static_assert(kPrefetch <= NQK, "prefetched slots are score-product slots");
+  // A loader wave spreads its DMAs over its matrix phase, one every
+  // kDmaStride slots, so the requests of the four loaders trickle into the
+  // memory pipeline instead of queueing behind each other.
+  constexpr int kDmaStride = NS / Lay::ISSUES;
+  static_assert(kDmaStride >= 1, "DMAs per matrix phase");
+  // A operand of slot s: for the output product two transposing reads give
+  // V^T rows db*32.. at keys kb*32 + 16hh + (0..7); for the score product
+  // one 16-byte read gives K row sigma(lq) of key block kb at k-step ks.
+  auto read_op = [&] __device__ (int s, const lds_u16_t* vt, const lds_u16_t* kt) __attribute__((always_inline))
+      -> bf16x8_t {
+    if (s < NQK) {
+      const int ks = s / kKeyBlocks, kb = s % kKeyBlocks;
       return *(const lds_bf16x8_t*)(kt + kread[ks] + kb * 32 * DQK);
-    };
+    }
+    const int q = s - NQK, kb = q / (2 * D_BLOCKS), hh = (q / D_BLOCKS) % 2, db = q % D_BLOCKS;
+    const lds_u16_t* vr = vt + vread[db] + (kb * 32 + 16 * hh) * DV;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr + 4 * DV));
+    const i16x4_t both[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8_t, both);
+  };
+  bf16x8_t op_pre[kPrefetch];
+  auto prefetch = [&] __device__ (const lds_u16_t* vt, const lds_u16_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) op_pre[s] = read_op(s, vt, kt);
+  };
+  // vt, kt: V tile of the output product and K tile of the score product;
+  // with DMA, this loader's requests for K tile tk -> kdst and V tile tv ->
+  // vdst are issued along the way.
+  auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* vt, const lds_u16_t* kt, int tk, int tv,
+                                lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+    constexpr bool DMA = decltype(dma_tag)::value;
     bf16x8_t op[NS];
 #pragma unroll
-    for (int s = 0; s < kPrefetch && s < NS; ++s) op[s] = read_op(s);
+    for (int s = 0; s < kPrefetch; ++s) op[s] = op_pre[s];
+    // P_{t-1} -> bf16 B operands and row sum
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          pb[kb][hh][jj] = pack_bf16x2(pf[kb][8 * hh + 2 * jj], pf[kb][8 * hh + 2 * jj + 1]);
+    {
+      float acc[4] = {pf[0][0], pf[0][1], pf[0][2], pf[0][3]};
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) acc[r % 4] += pf[kb][r];
+      l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
     const f32x16_t zero = {};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s + kPrefetch < NS) op[s + kPrefetch] = read_op(s + kPrefetch);
-      if (s < NPV) {
-        const int kb = s / (2 * D_BLOCKS), hh = (s / D_BLOCKS) % 2, db = s % D_BLOCKS;
+      if (s + kPrefetch < NS) op[s + kPrefetch] = read_op(s + kPrefetch, vt, kt);
+      if (s < NQK) {
+        const int ks = s / kKeyBlocks, kb = s % kKeyBlocks;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
+      } else {
+        const int q = s - NQK, kb = q / (2 * D_BLOCKS), hh = (q / D_BLOCKS) % 2, db = q % D_BLOCKS;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], __builtin_bit_cast(bf16x8_t, pb[kb][hh]),
                                                            oacc[db], 0, 0, 0);
-      } else {
-        const int q = s - NPV, ks = q / kKeyBlocks, kb = q % kKeyBlocks;
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
       }
+      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < Lay::ISSUES)
+        dma(s / kDmaStride, tk, tv, kdst, vdst);
     }
-    pin_matrix_schedule<0, NS, NPV>();
+    mx_raw = row_max();
+    // keep the row sum and max in this phase: left alone, the compiler sinks
+    // them to their first use, in the softmax phase
+    asm volatile("" : "+v"(l_part), "+v"(mx_raw));
+    pin_matrix_schedule<0, NS, NQK>();
   };
 
   // Does the softmax of tile t need masking for this wave?
@@ -442,17 +509,24 @@ void attn_fwd_kernel(FwdParams p) {
     return (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
   };
 
-  // ---- phases.  Group grp runs the matrix phase of tile j at phase 2j+grp
-  // (O += V[j-1] P[j-1], then S[j] = K[j] Q^T) and the softmax of tile j at
-  // phase 2j+1+grp.  K[j] and V[j-1] are read in phases 2j and 2j+1; the
-  // loads of K[j+1] and V[j] are issued at the start of phase 2j into the
-  // buffers last read in phases 2j-2 and 2j-1.
+  // ---- phases.  Iteration j (0 <= j <= ntiles) has two phases separated by
+  // barriers.  Group 0: phase 1 = matrix(j): O += P[j-1] V[j-1], S[j] = K[j]
+  // Q^T, issuing the DMAs of K[j+2] and V[j+1]; phase 2 = softmax(j).  Group 1
+  // runs one phase behind: phase 1 = softmax(j-1), phase 2 = matrix(j).
+  // K[t] and V[t] live in buffer t mod 3 (V[-1] is the zero-filled buffer 2).
+  // The DMAs issued in iteration j are awaited by their loaders before the
+  // mid barrier of iteration j+1, so their tiles are complete before either
+  // group prefetches from them; buffer (j+2) mod 3 was last read in iteration
+  // j-1, before the DMAs of iteration j refill it.
   // Softmax of tile t (in sacc): masks, row max, conditional rescale of O and
   // l, P = exp2(c s - m) as bf16 B operands, and the row sums.
   auto softmax = [&] __device__ (int t) __attribute__((always_inline)) {
     const int k0 = t * kBlockN;
-    // the mask only touches S; keeping it a separate branch leaves one path
-    // through the O rescale below
+    // Row max of the tile (raw logits; c > 0 so max commutes with scaling),
+    // computed by the matrix phase; a masked tile masks S and takes it again.
+    // Keeping the mask a separate branch leaves one path through the O
+    // rescale below.
+    float mx = mx_raw;
     if (needs_mask(t)) {
       const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
 #pragma unroll
@@ -462,17 +536,8 @@ void attn_fwd_kernel(FwdParams p) {
           const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
           if (key > lim) sacc[kb][r] = -__builtin_inff();
         }
+      mx = row_max();
     }
-    // row max of this tile (raw logits; c > 0 so max commutes with scaling)
-    float mx0 = sacc[0][0], mx1 = sacc[0][1];
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
-        mx0 = __builtin_fmaxf(mx0, sacc[kb][r]);
-        mx1 = __builtin_fmaxf(mx1, sacc[kb][r + 1]);
-      }
-    const float mx = max_with_partner(__builtin_fmaxf(mx0, mx1));
     const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
     if (t == 0) {
       m_run = m_tile;   // O and l are still zero: nothing to rescale
@@ -504,62 +569,71 @@ void attn_fwd_kernel(FwdParams p) {
         m_run = m_new;
       }
     }
+    // P = exp2(c s - m) in fp32; the next matrix phase rounds it to bf16 and
+    // adds it to the row sum (after the rescale of l above)
     const float neg_m = -m_run;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb) {
-      float pv[16];
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
-        pv[r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
-        acc[r % 4] += pv[r];
+        pf[kb][r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb[kb][hh][j] = pack_bf16x2(pv[8 * hh + 2 * j], pv[8 * hh + 2 * j + 1]);
-    }
-    l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
 
   // Every iteration runs the same matrix code, so the O accumulators keep
   // one register assignment: at j = 0 the output product multiplies zero P
-  // with the zero-filled V buffer 1, and at j = ntiles the score product of a
-  // stale K buffer is computed and dropped.  Causal tiles past a wave's
-  // diagonal go through the softmax fully masked (P = 0, no rescale), which
-  // leaves O, l and m exactly as skipping them would.
-  auto matrix_phase = [&] __device__ (int j) __attribute__((always_inline)) {
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    matrix(True{}, True{}, vbuf((j - 1) & 1), kbuf(j & 1));
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    n_tiles += (j < ntiles && j <= t_last) ? 1u : 0u;
-  };
+  // with the zero-filled V buffer, and at j = ntiles the score product of a
+  // stale K buffer is computed and dropped; DMAs past the last tile reload it
+  // into a free buffer.  Causal tiles past a wave's diagonal go through the
+  // softmax fully masked (P = 0, no rescale), which leaves O, l and m exactly
+  // as skipping them would.
   auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
     if (j >= 0 && j < ntiles) softmax(j);
   };
-  // Each group's loop is straight-line per iteration (two phases, two
-  // barriers); group 1 runs the softmax of the previous tile first.  Every
-  // wave runs ntiles + 1 iterations, so the barrier counts agree.
   auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
+    int b0 = 0;                                  // j mod 3
+    if (G == 0) prefetch(vbuf(2), kbuf(0));      // operands of matrix(0)
     for (int j = 0; j <= ntiles; ++j) {
-      if (j + 1 < ntiles) load_k(j + 1, kbuf((j + 1) & 1));
-      if (j < ntiles) load_v(j, vbuf(j & 1));
-      if (G == 0) matrix_phase(j);
-      else softmax_phase(j - 1);
-      phase_barrier<false>();
-      if (G == 0) softmax_phase(j);
-      else matrix_phase(j);
-      phase_barrier<true>();    // K[j+1] and V[j] complete: first read next phase
+      const int bm1 = (b0 == 0) ? 2 : b0 - 1;    // (j - 1) mod 3 = (j + 2) mod 3
+      const int bp1 = (b0 == 2) ? 0 : b0 + 1;    // (j + 1) mod 3
+      if (G == 0) {
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        matrix(True{}, vbuf(bm1), kbuf(b0), min(j + 2, ntiles - 1), min(j + 1, ntiles - 1), kbuf(bm1), vbuf(bp1));
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        dma_wait_barrier<Lay::ISSUES>();         // K[j+1], V[j] have landed
+        softmax_phase(j);
+        prefetch(vbuf(b0), kbuf(bp1));           // operands of matrix(j+1)
+        barrier();
+      } else {
+        softmax_phase(j - 1);
+        prefetch(vbuf(bm1), kbuf(b0));           // operands of matrix(j)
+        barrier();
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        matrix(False{}, vbuf(bm1), kbuf(b0), 0, 0, kbuf(bm1), vbuf(bp1));
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        barrier();
+      }
+      n_tiles += (j < ntiles && j <= t_last) ? 1u : 0u;
+      b0 = bp1;
     }
   };
-  // V buffer 1 is read (times P = 0) before its first fill
-  for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
-  load_k(0, kbuf(0));
-  phase_barrier<true>();
+  // Prologue: V buffer 2 is read (times P = 0) by matrix(0); the loaders fetch
+  // K[0], K[1] and V[0] and wait for them before the first barrier.
+  for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(2))[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (grp == 0) {
+#pragma unroll
+    for (int d = 0; d < Lay::ISSUES; ++d) dma(d, 0, 0, kbuf(0), vbuf(0));
+#pragma unroll
+    for (int d = 0; d < Lay::K_ISSUES; ++d) dma(d, min(1, ntiles - 1), 0, kbuf(1), vbuf(0));
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
   if (grp == 0) run(Grp0{});
   else run(Grp1{});
+  dma_wait_all();   // the last iteration's DMAs land before the workgroup's LDS is released
 
   // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2
   const float l_tot = sum_with_partner(l_part);
