@@ -379,18 +379,16 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- per-wave state: S^T of the tile between its two phases, its raw row
-  // max, P^T in fp32 from the softmax until the next matrix phase and as bf16
-  // B operands, O^T accumulators, running max (log2 units) and lane-partial
-  // row sum
+  // ---- per-wave state: S^T of the tile between its two phases and its raw
+  // row max, P^T as bf16 B operands (zero before the first softmax), O^T
+  // accumulators, running max (log2 units) and lane-partial row sum
   f32x16_t sacc[kKeyBlocks];
-  f32x16_t pf[kKeyBlocks];
+  float mx_raw = -__builtin_inff();
+  u32x4_t pb[kKeyBlocks][2];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pf[kb][r] = 0.0f;
-  float mx_raw = -__builtin_inff();
-  u32x4_t pb[kKeyBlocks][2];
+    for (int hh = 0; hh < 2; ++hh) pb[kb][hh] = u32x4_t{0u, 0u, 0u, 0u};
   f32x16_t oacc[D_BLOCKS];
 #pragma unroll
   for (int db = 0; db < D_BLOCKS; ++db)
@@ -400,6 +398,7 @@ void attn_fwd_kernel(FwdParams p) {
   float l_part = 0.0f;
   const float c = p.c;
   const float tau = p.tau;
+  const float tau_dec = __builtin_fmaxf(tau, 0.0f);
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
 
   // Row max of S^T over the tile: lane-local over its 32 keys, then with the
@@ -418,10 +417,9 @@ void attn_fwd_kernel(FwdParams p) {
   // One matrix phase as a single stream of MFMA slots: first the score
   // product S^T = K_t Q^T (slots (ks, kb)), then the output product
   // O^T += V_{t-1}^T P_{t-1}^T (slots (kb, hh, db), db fastest, so neighbours
-  // accumulate into different blocks).  Alongside the MFMAs the wave rounds
-  // P_{t-1} to bf16 and adds it to the row sum, then takes the row max of
-  // S_t: VALU work that issues while the matrix core is busy, taken off the
-  // softmax phase of the other wave on the SIMD.  The LDS operand of slot s + kPrefetch is read before
+  // accumulate into different blocks).  Under the output product's MFMAs the
+  // wave takes the row max of S_t, a chain of dependent VALU operations that
+  // would otherwise stall the softmax phase.  The LDS operand of slot s + kPrefetch is read before
   // the MFMA of slot s, and pin_matrix_schedule fixes that order, so each read
   // has several MFMAs (32 cycles each) to return; the operands of the first
   // kPrefetch slots are read (prefetch) at the end of the wave's previous
@@ -465,22 +463,6 @@ void attn_fwd_kernel(FwdParams p) {
     bf16x8_t op[NS];
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) op[s] = op_pre[s];
-    // P_{t-1} -> bf16 B operands and row sum
-#pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          pb[kb][hh][jj] = pack_bf16x2(pf[kb][8 * hh + 2 * jj], pf[kb][8 * hh + 2 * jj + 1]);
-    {
-      float acc[4] = {pf[0][0], pf[0][1], pf[0][2], pf[0][3]};
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) acc[r % 4] += pf[kb][r];
-      l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
     const f32x16_t zero = {};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -497,9 +479,9 @@ void attn_fwd_kernel(FwdParams p) {
         dma(s / kDmaStride, tk, tv, kdst, vdst);
     }
     mx_raw = row_max();
-    // keep the row sum and max in this phase: left alone, the compiler sinks
-    // them to their first use, in the softmax phase
-    asm volatile("" : "+v"(l_part), "+v"(mx_raw));
+    // keep the row max in this phase: left alone, the compiler sinks it to
+    // its first use, in the softmax phase
+    asm volatile("" : "+v"(mx_raw));
     pin_matrix_schedule<0, NS, NQK>();
   };
 
@@ -539,46 +521,55 @@ void attn_fwd_kernel(FwdParams p) {
       mx = row_max();
     }
     const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-    if (t == 0) {
-      m_run = m_tile;   // O and l are still zero: nothing to rescale
-    } else {
-      bool need;
-      float m_new;
-      if (tau < 0.0f) {                 // classic online softmax: always rescale
-        m_new = __builtin_fmaxf(m_run, m_tile);
-        need = true;
-      } else {
-        need = m_tile > m_run + tau;
-        m_new = need ? m_tile : m_run;
-      }
-      if (row_valid && g == 0 && t <= t_last) {
-        n_considered += 1;
-        n_taken += need ? 1u : 0u;
-      }
-      if (tau < 0.0f || __builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
+    // Rescale when the tile max exceeds the running max by more than tau
+    // (log2 units).  tau < 0 asks for the classic rule, rescaling whenever
+    // the max grows; a tile whose max did not grow would be rescaled by
+    // exp2(0) = 1, an exact no-op, so both rules are taken here as
+    // "m_tile > m_run + max(tau, 0)".  On the first tile m_run = -inf, so
+    // every lane rescales its still-zero O and l (alpha = 0).
+    const bool need = m_tile > m_run + tau_dec;
+    const bool counted = row_valid && g == 0 && t >= 1 && t <= t_last;
+    n_considered += counted ? 1u : 0u;
+    n_taken += (counted && (need || tau < 0.0f)) ? 1u : 0u;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? __builtin_fmaxf(m_run, m_tile) : m_run;
+      const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
 #pragma unroll
-        for (int db = 0; db < D_BLOCKS; ++db)
+      for (int db = 0; db < D_BLOCKS; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = oacc[db][r];
-            scale_in_place(x, alpha);
-            oacc[db][r] = x;
-          }
-        l_part *= alpha;
-        m_run = m_new;
-      }
+        for (int r = 0; r < 16; ++r) {
+          float x = oacc[db][r];
+          scale_in_place(x, alpha);
+          oacc[db][r] = x;
+        }
+      l_part *= alpha;
+      m_run = m_new;
     }
-    // P = exp2(c s - m) in fp32; the next matrix phase rounds it to bf16 and
-    // adds it to the row sum (after the rescale of l above)
+    // P = exp2(c s - m) in fp32 (all FMAs before the exponentials, so no exp
+    // waits on the FMA just before it), then bf16 B operands and the row sum.
     const float neg_m = -m_run;
 #pragma unroll
     for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float y = __builtin_fmaf(sacc[kb][r], c, neg_m);
-        pf[kb][r] = ((r % 8) < NPOLY / 2) ? exp2_poly(y) : exp2_hw(y);
-      }
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_fmaf(sacc[kb][r], c, neg_m);
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[kb][r] = ((r % 8) < NPOLY / 2) ? exp2_poly(sacc[kb][r]) : exp2_hw(sacc[kb][r]);
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          pb[kb][hh][jj] = pack_bf16x2(sacc[kb][8 * hh + 2 * jj], sacc[kb][8 * hh + 2 * jj + 1]);
+    float acc[4] = {sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]};
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) acc[r % 4] += sacc[kb][r];
+    l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
 
   // Every iteration runs the same matrix code, so the O accumulators keep
