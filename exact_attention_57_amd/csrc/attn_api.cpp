@@ -77,6 +77,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   const int rows = attn::query_block_rows();
   const int64_t nqb = ((int64_t)N + rows - 1) / rows;
   if (B > kMaxGridYZ || nqb > kMaxGridYZ) return ATTN_ERR_SHAPE;
+  // the longest-first schedule launches one workgroup per (head, sequence, query block)
+  if ((int64_t)H * B * nqb > INT32_MAX) return ATTN_ERR_SHAPE;
   // token indices are 32-bit inside the kernel
   if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
 

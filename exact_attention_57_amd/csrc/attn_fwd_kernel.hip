@@ -83,6 +83,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
 constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kKeyBlocks = kBlockN / 32;
+constexpr int kXcds = 8;                         // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ float exp2_hw(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
@@ -272,10 +273,27 @@ void attn_fwd_kernel(FwdParams p) {
   const int g = lane / 32;       // lane half
   const int lq = lane % 32;      // query column
 
-  // ---- work decode: blockIdx = (head, sequence, query-block slot)
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int qblk = (p.schedule == 0) ? (p.n_qblocks - 1 - (int)blockIdx.z) : (int)blockIdx.z;
+  // ---- work decode.  Longest-first schedule: a 1-D grid whose workgroups
+  // the hardware deals to the 8 XCDs in turn (workgroup i to XCD i mod 8).
+  // XCD x takes a contiguous run of a list ordered by (sequence, head) pair,
+  // head-major so that every XCD sees every sequence length, and by query
+  // block longest-first within a pair: the query blocks of a pair then run
+  // side by side on one XCD and share its L2 for the pair's K and V tiles.
+  // Natural schedule: blockIdx = (head, sequence, query block).
+  int h, b, qblk;
+  if (p.schedule == 0) {
+    const int W = p.H * p.B * p.n_qblocks;
+    const int i = blockIdx.x, x = i % kXcds, slot = i / kXcds;
+    const int g = x * (W / kXcds) + min(x, W % kXcds) + slot;
+    const int pair = g / p.n_qblocks;
+    qblk = p.n_qblocks - 1 - (g - pair * p.n_qblocks);
+    h = pair / p.B;
+    b = pair - h * p.B;
+  } else {
+    h = blockIdx.x;
+    b = blockIdx.y;
+    qblk = blockIdx.z;
+  }
   int seq0, L, T;
   if (p.cu_seqlens) {
     seq0 = p.cu_seqlens[b];
@@ -667,7 +685,7 @@ __global__ void exp2_debug_kernel(const float* __restrict__ x, float* __restrict
 
 template <int DQK, int DV, bool CAUSAL>
 static hipError_t launch_poly(const FwdParams& p, int npoly, hipStream_t s) {
-  const dim3 grid(p.H, p.B, p.n_qblocks);
+  const dim3 grid = (p.schedule == 0) ? dim3(p.H * p.B * p.n_qblocks) : dim3(p.H, p.B, p.n_qblocks);
   const dim3 block(kThreads);
   switch (npoly) {
     case 0: hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, CAUSAL, 0>), grid, block, 0, s, p); break;

@@ -27,7 +27,10 @@
  *     hardware exp2.
  * The tile order follows the causal/varlen load-balancing scheduler idea of
  * the newton.com.tw wiki "FlashAttention-4", core-technology section:
- * query blocks with the most key tiles are dispatched first.
+ * query blocks with the most key tiles are dispatched first.  On MI355X the
+ * default order also keeps all query blocks of one (sequence, head) pair on
+ * one XCD, dispatched one after another, so that they share that XCD's L2
+ * for the pair's K and V.
  *
  * ------------------------------------------------------------------ layouts
  *   q, k : bf16 [T, H, d_qk]   token-major, heads interleaved, contiguous
@@ -90,7 +93,10 @@ typedef struct attn_fwd_opts {
   /* Sixteenths of the exponentials computed with the software exp2:
    * one of 0, 2, 4, 8 (0, 1/8, 1/4, 1/2).  Default 0. */
   int poly_exp_sixteenths;
-  /* ATTN_SCHEDULE_LONGEST_FIRST (default) or ATTN_SCHEDULE_NATURAL. */
+  /* ATTN_SCHEDULE_LONGEST_FIRST (default: per (sequence, head) pair,
+   * longest query blocks first, pairs spread over the XCDs) or
+   * ATTN_SCHEDULE_NATURAL (grid order).  Results are identical bit for bit;
+   * only the speed differs. */
   int schedule;
   /* Optional DEVICE uint64[4] the kernel ADDS to (caller zeroes it):
    * [0] row-tile pairs where a rescale was considered (after a row's first
