@@ -49,7 +49,7 @@ int attn_version(void) { return kVersion; }
 int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile, int* rows_per_wave) {
   if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
   if (rows_per_item) *rows_per_item = attn::query_block_rows();
-  if (keys_per_tile) *keys_per_tile = attn::keys_per_tile();
+  if (keys_per_tile) *keys_per_tile = attn::keys_per_tile(d_qk);
   if (rows_per_wave) *rows_per_wave = attn::rows_per_wave();
   return ATTN_OK;
 }

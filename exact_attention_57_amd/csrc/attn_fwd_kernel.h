@@ -25,7 +25,7 @@ struct FwdParams {
 };
 
 int query_block_rows();
-int keys_per_tile();
+int keys_per_tile(int d_qk);
 int rows_per_wave();
 hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int npoly, hipStream_t s);
 hipError_t launch_exp2_debug(const float* x, float* y, int n, int use_poly, hipStream_t s);

@@ -81,8 +81,13 @@ constexpr int kWaves = 8;              // two per SIMD: one per ping-pong group
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
-constexpr int kBlockN = 64;                      // keys per tile
-constexpr int kKeyBlocks = kBlockN / 32;
+// Keys per tile: 128 where the registers allow it (d_qk <= 128), else 64.
+// Larger tiles halve the per-tile cost of the phase barriers and the
+// softmax's row-wide steps.
+#ifndef ATTN_BLOCK_N_SMALL_D
+#define ATTN_BLOCK_N_SMALL_D 128
+#endif
+constexpr int block_n(int d_qk) { return d_qk <= 128 ? ATTN_BLOCK_N_SMALL_D : 64; }
 constexpr int kXcds = 8;                         // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ float exp2_hw(float x) {
@@ -155,16 +160,33 @@ struct VSwz {
 
 // Tiles are filled by the four group-0 waves, during their matrix phases.
 constexpr int kLoaders = kWaves / 2;
-constexpr int kBufs = 3;                 // K and V tile buffers in LDS
+constexpr int kKBufs = 3;                // K tile buffers in LDS
+constexpr int kVBufs = 2;                // V tile buffers in LDS
 
-template <int DQK, int DV>
+// Smallest number p of consecutive 1 KB DMA requests (64 chunks of 16 bytes)
+// after which a loader's chunk pattern repeats: a whole number of rows of R
+// chunks that is also a multiple of the swizzle period.  Request i then uses
+// the lane offset of request i mod p, shifted by whole rows.
+constexpr int dma_period(int R, int swizzle_rows) {
+  for (int p = 1; p < 64; ++p)
+    if ((p * 64) % R == 0 && ((p * 64 / R) % swizzle_rows) == 0) return p;
+  return 64;
+}
+
+template <int DQK, int DV, int BN>
 struct TileLayout {
-  static constexpr int K_ELEMS = kBlockN * DQK;          // dense K tile
-  static constexpr int V_ELEMS = kBlockN * DV;           // dense V tile
+  static constexpr int K_ELEMS = BN * DQK;               // dense K tile
+  static constexpr int V_ELEMS = BN * DV;                // dense V tile
   static constexpr int K_ISSUES = (K_ELEMS / 512) / kLoaders;   // 1 KB DMAs per loader wave per K tile
   static constexpr int V_ISSUES = (V_ELEMS / 512) / kLoaders;
   static constexpr int ISSUES = K_ISSUES + V_ISSUES;
   static_assert((K_ELEMS / 512) % kLoaders == 0 && (V_ELEMS / 512) % kLoaders == 0, "tile split");
+  static constexpr int K_PERIOD = dma_period(DQK / 8, 16);
+  static constexpr int V_PERIOD = dma_period(DV / 8, 4);
+  static constexpr int K_OFFS = K_ISSUES < K_PERIOD ? K_ISSUES : K_PERIOD;   // lane offsets kept
+  static constexpr int V_OFFS = V_ISSUES < V_PERIOD ? V_ISSUES : V_PERIOD;
+  static constexpr int LDS_ELEMS = kKBufs * K_ELEMS + kVBufs * V_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
 };
 
 // One buffer_load_dwordx4 ... lds request: copies, for every lane, the
@@ -253,17 +275,19 @@ template <int DQK, int DV, bool CAUSAL, int NPOLY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
-  using Lay = TileLayout<DQK, DV>;
+  constexpr int BN = block_n(DQK);               // keys per tile
+  constexpr int KB = BN / 32;                      // 32-key blocks per tile
+  using Lay = TileLayout<DQK, DV, BN>;
   constexpr int QK_STEPS = DQK / 16;             // MFMA k-steps for S^T
   constexpr int D_BLOCKS = DV / 32;              // 32-row blocks of O^T
   constexpr int RK = DQK / 8;                    // 16-byte chunks per K row
   constexpr int RV = DV / 8;                     // 16-byte chunks per V row
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[kBufs * Lay::K_ELEMS + kBufs * Lay::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[Lay::LDS_ELEMS];
   lds_u16_t* const lds = (lds_u16_t*)smem;
   auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * Lay::K_ELEMS; };
   auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) {
-    return lds + kBufs * Lay::K_ELEMS + i * Lay::V_ELEMS;
+    return lds + kKBufs * Lay::K_ELEMS + i * Lay::V_ELEMS;
   };
 
   const int tid = threadIdx.x;
@@ -307,7 +331,7 @@ void attn_fwd_kernel(FwdParams p) {
   const int q0 = qblk * kBlockM;
   if (q0 >= L) return;  // uniform over the workgroup
   const int kend = CAUSAL ? min(L, q0 + kBlockM) : L;
-  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  const int ntiles = (kend + BN - 1) / BN;
 
   const int H = p.H;
   const int64_t qk_row = (int64_t)H * DQK;   // elements between consecutive tokens
@@ -315,7 +339,7 @@ void attn_fwd_kernel(FwdParams p) {
 
   const int qw0 = q0 + kRowsPerWave * wave;   // first query row of this wave
   // last key tile with a key visible to some row of this wave
-  const int t_last = CAUSAL ? min(ntiles - 1, (qw0 + kRowsPerWave - 1) / kBlockN) : ntiles - 1;
+  const int t_last = CAUSAL ? min(ntiles - 1, (qw0 + kRowsPerWave - 1) / BN) : ntiles - 1;
   const int qrow = qw0 + lq;
   const bool row_valid = qrow < L;
 
@@ -344,30 +368,38 @@ void attn_fwd_kernel(FwdParams p) {
   const uint32_t k_bytes = (uint32_t)((L - 1) * (int64_t)qk_row * 2 + DQK * 2);
   const uint32_t v_bytes = (uint32_t)((L - 1) * (int64_t)v_row * 2 + DV * 2);
   // lane byte offsets (within a tile) of the chunks this lane loads when its
-  // wave is loader lw (group 1 computes them but issues no DMA)
+  // wave is loader lw (group 1 computes them but issues no DMA); requests
+  // past the pattern's period reuse them shifted by whole rows
   const int lw = wave % kLoaders;
-  uint32_t koff[Lay::K_ISSUES], voff[Lay::V_ISSUES];
+  uint32_t koff[Lay::K_OFFS], voff[Lay::V_OFFS];
 #pragma unroll
-  for (int i = 0; i < Lay::K_ISSUES; ++i) {
+  for (int i = 0; i < Lay::K_OFFS; ++i) {
     const int slot = (lw * Lay::K_ISSUES + i) * 64 + lane;
     const int row = slot / RK, pos = slot % RK;
     koff[i] = (uint32_t)row * k_rowbytes + (uint32_t)(pos ^ KSwz<DQK>::f(row)) * 16u;
   }
 #pragma unroll
-  for (int i = 0; i < Lay::V_ISSUES; ++i) {
+  for (int i = 0; i < Lay::V_OFFS; ++i) {
     const int slot = (lw * Lay::V_ISSUES + i) * 64 + lane;
     const int row = slot / RV, pos = slot % RV;
     voff[i] = (uint32_t)row * v_rowbytes + (uint32_t)(pos ^ VSwz<DV>::f(row)) * 16u;
   }
+  const uint32_t k_period_bytes = (uint32_t)(Lay::K_PERIOD * 64 / RK) * k_rowbytes;
+  const uint32_t v_period_bytes = (uint32_t)(Lay::V_PERIOD * 64 / RV) * v_rowbytes;
   const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
   const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
-  // DMA d (0 <= d < ISSUES) of this loader's share of K tile tk then V tile tv
+  // DMA d (0 <= d < ISSUES) of this loader's share of V tile tv, then of K
+  // tile tk (V first: it is awaited one phase earlier than K)
   auto dma = [&] __device__ (int d, int tk, int tv, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
-    if (d < Lay::K_ISSUES) {
-      dma_chunk(k_rsrc, koff[d], (uint32_t)(tk * kBlockN) * k_rowbytes, kdst + (lw * Lay::K_ISSUES + d) * 512);
+    if (d < Lay::V_ISSUES) {
+      dma_chunk(v_rsrc, voff[d % Lay::V_PERIOD],
+                (uint32_t)(tv * BN) * v_rowbytes + (uint32_t)(d / Lay::V_PERIOD) * v_period_bytes,
+                vdst + (lw * Lay::V_ISSUES + d) * 512);
     } else {
-      const int e = d - Lay::K_ISSUES;
-      dma_chunk(v_rsrc, voff[e], (uint32_t)(tv * kBlockN) * v_rowbytes, vdst + (lw * Lay::V_ISSUES + e) * 512);
+      const int e = d - Lay::V_ISSUES;
+      dma_chunk(k_rsrc, koff[e % Lay::K_PERIOD],
+                (uint32_t)(tk * BN) * k_rowbytes + (uint32_t)(e / Lay::K_PERIOD) * k_period_bytes,
+                kdst + (lw * Lay::K_ISSUES + e) * 512);
     }
   };
 
@@ -400,11 +432,11 @@ void attn_fwd_kernel(FwdParams p) {
   // ---- per-wave state: S^T of the tile between its two phases and its raw
   // row max, P^T as bf16 B operands (zero before the first softmax), O^T
   // accumulators, running max (log2 units) and lane-partial row sum
-  f32x16_t sacc[kKeyBlocks];
+  f32x16_t sacc[KB];
   float mx_raw = -__builtin_inff();
-  u32x4_t pb[kKeyBlocks][2];
+  u32x4_t pb[KB][2];
 #pragma unroll
-  for (int kb = 0; kb < kKeyBlocks; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) pb[kb][hh] = u32x4_t{0u, 0u, 0u, 0u};
   f32x16_t oacc[D_BLOCKS];
@@ -424,7 +456,7 @@ void attn_fwd_kernel(FwdParams p) {
   auto row_max = [&] __device__ () __attribute__((always_inline)) -> float {
     float mx0 = sacc[0][0], mx1 = sacc[0][1];
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
         mx0 = __builtin_fmaxf(mx0, sacc[kb][r]);
@@ -442,8 +474,8 @@ void attn_fwd_kernel(FwdParams p) {
   // has several MFMAs (32 cycles each) to return; the operands of the first
   // kPrefetch slots are read (prefetch) at the end of the wave's previous
   // phase, so the stream starts without waiting for LDS.
-  constexpr int NPV = kKeyBlocks * 2 * D_BLOCKS;
-  constexpr int NQK = QK_STEPS * kKeyBlocks;
+  constexpr int NPV = KB * 2 * D_BLOCKS;
+  constexpr int NQK = QK_STEPS * KB;
   constexpr int NS = NPV + NQK;
   static_assert(kPrefetch <= NQK, "prefetched slots are score-product slots");
   // A loader wave spreads its DMAs over its matrix phase, one every
@@ -457,7 +489,7 @@ void attn_fwd_kernel(FwdParams p) {
   auto read_op = [&] __device__ (int s, const lds_u16_t* vt, const lds_u16_t* kt) __attribute__((always_inline))
       -> bf16x8_t {
     if (s < NQK) {
-      const int ks = s / kKeyBlocks, kb = s % kKeyBlocks;
+      const int ks = s / KB, kb = s % KB;
       return *(const lds_bf16x8_t*)(kt + kread[ks] + kb * 32 * DQK);
     }
     const int q = s - NQK, kb = q / (2 * D_BLOCKS), hh = (q / D_BLOCKS) % 2, db = q % D_BLOCKS;
@@ -486,7 +518,7 @@ void attn_fwd_kernel(FwdParams p) {
     for (int s = 0; s < NS; ++s) {
       if (s + kPrefetch < NS) op[s + kPrefetch] = read_op(s + kPrefetch, vt, kt);
       if (s < NQK) {
-        const int ks = s / kKeyBlocks, kb = s % kKeyBlocks;
+        const int ks = s / KB, kb = s % KB;
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
       } else {
         const int q = s - NQK, kb = q / (2 * D_BLOCKS), hh = (q / D_BLOCKS) % 2, db = q % D_BLOCKS;
@@ -505,23 +537,24 @@ void attn_fwd_kernel(FwdParams p) {
 
   // Does the softmax of tile t need masking for this wave?
   auto needs_mask = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * kBlockN;
-    return (k0 + kBlockN > L) || (CAUSAL && k0 + kBlockN - 1 > qw0);
+    const int k0 = t * BN;
+    return (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > qw0);
   };
 
   // ---- phases.  Iteration j (0 <= j <= ntiles) has two phases separated by
-  // barriers.  Group 0: phase 1 = matrix(j): O += P[j-1] V[j-1], S[j] = K[j]
-  // Q^T, issuing the DMAs of K[j+2] and V[j+1]; phase 2 = softmax(j).  Group 1
-  // runs one phase behind: phase 1 = softmax(j-1), phase 2 = matrix(j).
-  // K[t] and V[t] live in buffer t mod 3 (V[-1] is the zero-filled buffer 2).
-  // The DMAs issued in iteration j are awaited by their loaders before the
-  // mid barrier of iteration j+1, so their tiles are complete before either
-  // group prefetches from them; buffer (j+2) mod 3 was last read in iteration
-  // j-1, before the DMAs of iteration j refill it.
+  // barriers.  Group 0: phase 1 = matrix(j): S[j] = K[j] Q^T, O += P[j-1]
+  // V[j-1], issuing the DMAs of V[j] and K[j+2]; phase 2 = softmax(j).  Group
+  // 1 runs one phase behind: phase 1 = softmax(j-1), phase 2 = matrix(j).
+  // K[t] lives in K buffer t mod 3, V[t] in V buffer t mod 2 (V[-1] is the
+  // zero-filled V buffer 1).  The loaders wait for V[j] before the end
+  // barrier of iteration j and for K[j+2] before the mid barrier of
+  // iteration j+1, so every tile is complete before any wave reads or
+  // prefetches it; the buffers the DMAs of iteration j refill (K[j-1],
+  // V[j-2]) were last read in iteration j-1.
   // Softmax of tile t (in sacc): masks, row max, conditional rescale of O and
   // l, P = exp2(c s - m) as bf16 B operands, and the row sums.
   auto softmax = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * kBlockN;
+    const int k0 = t * BN;
     // Row max of the tile (raw logits; c > 0 so max commutes with scaling),
     // computed by the matrix phase; a masked tile masks S and takes it again.
     // Keeping the mask a separate branch leaves one path through the O
@@ -530,7 +563,7 @@ void attn_fwd_kernel(FwdParams p) {
     if (needs_mask(t)) {
       const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);   // last visible key
 #pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
@@ -567,16 +600,16 @@ void attn_fwd_kernel(FwdParams p) {
     // waits on the FMA just before it), then bf16 B operands and the row sum.
     const float neg_m = -m_run;
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_fmaf(sacc[kb][r], c, neg_m);
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         sacc[kb][r] = ((r % 8) < NPOLY / 2) ? exp2_poly(sacc[kb][r]) : exp2_hw(sacc[kb][r]);
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -584,7 +617,7 @@ void attn_fwd_kernel(FwdParams p) {
           pb[kb][hh][jj] = pack_bf16x2(sacc[kb][8 * hh + 2 * jj], sacc[kb][8 * hh + 2 * jj + 1]);
     float acc[4] = {sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]};
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) acc[r % 4] += sacc[kb][r];
     l_part += (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -603,24 +636,25 @@ void attn_fwd_kernel(FwdParams p) {
   auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
     int b0 = 0;                                  // j mod 3
-    if (G == 0) prefetch(vbuf(2), kbuf(0));      // operands of matrix(0)
+    if (G == 0) prefetch(vbuf(1), kbuf(0));      // operands of matrix(0)
     for (int j = 0; j <= ntiles; ++j) {
       const int bm1 = (b0 == 0) ? 2 : b0 - 1;    // (j - 1) mod 3 = (j + 2) mod 3
       const int bp1 = (b0 == 2) ? 0 : b0 + 1;    // (j + 1) mod 3
+      const int vc = j & 1, vp = vc ^ 1;         // V buffers of V[j] and V[j-1]
       if (G == 0) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        matrix(True{}, vbuf(bm1), kbuf(b0), min(j + 2, ntiles - 1), min(j + 1, ntiles - 1), kbuf(bm1), vbuf(bp1));
+        matrix(True{}, vbuf(vp), kbuf(b0), min(j + 2, ntiles - 1), min(j, ntiles - 1), kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        dma_wait_barrier<Lay::ISSUES>();         // K[j+1], V[j] have landed
+        dma_wait_barrier<Lay::ISSUES>();         // K[j+1] has landed
         softmax_phase(j);
-        prefetch(vbuf(b0), kbuf(bp1));           // operands of matrix(j+1)
-        barrier();
+        prefetch(vbuf(vc), kbuf(bp1));           // operands of matrix(j+1)
+        dma_wait_barrier<Lay::K_ISSUES>();       // V[j] has landed
       } else {
         softmax_phase(j - 1);
-        prefetch(vbuf(bm1), kbuf(b0));           // operands of matrix(j)
+        prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
         barrier();
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        matrix(False{}, vbuf(bm1), kbuf(b0), 0, 0, kbuf(bm1), vbuf(bp1));
+        matrix(False{}, vbuf(vp), kbuf(b0), 0, 0, kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         barrier();
       }
@@ -628,14 +662,14 @@ void attn_fwd_kernel(FwdParams p) {
       b0 = bp1;
     }
   };
-  // Prologue: V buffer 2 is read (times P = 0) by matrix(0); the loaders fetch
-  // K[0], K[1] and V[0] and wait for them before the first barrier.
-  for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(2))[i] = u32x4_t{0u, 0u, 0u, 0u};
+  // Prologue: V buffer 1 is read (times P = 0) by matrix(0); the loaders fetch
+  // K[0] and K[1] and wait for them before the first barrier.
+  for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
   if (grp == 0) {
 #pragma unroll
-    for (int d = 0; d < Lay::ISSUES; ++d) dma(d, 0, 0, kbuf(0), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, 0, 0, kbuf(0), vbuf(0));
 #pragma unroll
-    for (int d = 0; d < Lay::K_ISSUES; ++d) dma(d, min(1, ntiles - 1), 0, kbuf(1), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, min(1, ntiles - 1), 0, kbuf(1), vbuf(0));
   }
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -703,7 +737,7 @@ static hipError_t launch_dims(const FwdParams& p, bool causal, int npoly, hipStr
 }
 
 int query_block_rows() { return kBlockM; }
-int keys_per_tile() { return kBlockN; }
+int keys_per_tile(int d_qk) { return block_n(d_qk); }
 int rows_per_wave() { return kRowsPerWave; }
 
 hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int npoly, hipStream_t s) {
