@@ -81,13 +81,17 @@ constexpr int kWaves = 8;              // two per SIMD: one per ping-pong group
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
-// Keys per tile: 128 where the registers allow it (d_qk <= 128), else 64.
+// Keys per tile: 128 where the registers allow it (d_qk <= 128), else 64
+// (96 also fits at d_qk = 192 but measured slower).
 // Larger tiles halve the per-tile cost of the phase barriers and the
 // softmax's row-wide steps.
 #ifndef ATTN_BLOCK_N_SMALL_D
 #define ATTN_BLOCK_N_SMALL_D 128
 #endif
-constexpr int block_n(int d_qk) { return d_qk <= 128 ? ATTN_BLOCK_N_SMALL_D : 64; }
+#ifndef ATTN_BLOCK_N_LARGE_D
+#define ATTN_BLOCK_N_LARGE_D 64
+#endif
+constexpr int block_n(int d_qk) { return d_qk <= 128 ? ATTN_BLOCK_N_SMALL_D : ATTN_BLOCK_N_LARGE_D; }
 constexpr int kXcds = 8;                         // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ float exp2_hw(float x) {
