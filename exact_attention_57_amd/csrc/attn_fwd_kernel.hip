@@ -392,17 +392,26 @@ void attn_fwd_kernel(FwdParams p) {
   const uint32_t v_period_bytes = (uint32_t)(Lay::V_PERIOD * 64 / RV) * v_rowbytes;
   const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
   const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
-  // DMA d (0 <= d < ISSUES) of this loader's share of V tile tv, then of K
-  // tile tk (V first: it is awaited one phase earlier than K)
-  auto dma = [&] __device__ (int d, int tk, int tv, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+  // Byte offset of tile t in the K or V resource; a tile past the last one
+  // starts at the resource's end, so its DMAs return zeros without touching
+  // memory.
+  auto k_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BN) * k_rowbytes : k_bytes;
+  };
+  auto v_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BN) * v_rowbytes : v_bytes;
+  };
+  // DMA d (0 <= d < ISSUES) of this loader's share of the V tile at byte
+  // offset tv, then of the K tile at tk (V first: it is awaited one phase
+  // earlier than K)
+  auto dma = [&] __device__ (int d, uint32_t tk, uint32_t tv, lds_u16_t* kdst, lds_u16_t* vdst)
+      __attribute__((always_inline)) {
     if (d < Lay::V_ISSUES) {
-      dma_chunk(v_rsrc, voff[d % Lay::V_PERIOD],
-                (uint32_t)(tv * BN) * v_rowbytes + (uint32_t)(d / Lay::V_PERIOD) * v_period_bytes,
+      dma_chunk(v_rsrc, voff[d % Lay::V_PERIOD], tv + (uint32_t)(d / Lay::V_PERIOD) * v_period_bytes,
                 vdst + (lw * Lay::V_ISSUES + d) * 512);
     } else {
       const int e = d - Lay::V_ISSUES;
-      dma_chunk(k_rsrc, koff[e % Lay::K_PERIOD],
-                (uint32_t)(tk * BN) * k_rowbytes + (uint32_t)(e / Lay::K_PERIOD) * k_period_bytes,
+      dma_chunk(k_rsrc, koff[e % Lay::K_PERIOD], tk + (uint32_t)(e / Lay::K_PERIOD) * k_period_bytes,
                 kdst + (lw * Lay::K_ISSUES + e) * 512);
     }
   };
@@ -511,7 +520,7 @@ void attn_fwd_kernel(FwdParams p) {
   // vt, kt: V tile of the output product and K tile of the score product;
   // with DMA, this loader's requests for K tile tk -> kdst and V tile tv ->
   // vdst are issued along the way.
-  auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* vt, const lds_u16_t* kt, int tk, int tv,
+  auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* vt, const lds_u16_t* kt, uint32_t tk, uint32_t tv,
                                 lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
     constexpr bool DMA = decltype(dma_tag)::value;
     bf16x8_t op[NS];
@@ -630,8 +639,8 @@ void attn_fwd_kernel(FwdParams p) {
   // Every iteration runs the same matrix code, so the O accumulators keep
   // one register assignment: at j = 0 the output product multiplies zero P
   // with the zero-filled V buffer, and at j = ntiles the score product of a
-  // stale K buffer is computed and dropped; DMAs past the last tile reload it
-  // into a free buffer.  Causal tiles past a wave's diagonal go through the
+  // stale K buffer is computed and dropped; DMAs past the last tile fill a
+  // free buffer with zeros.  Causal tiles past a wave's diagonal go through the
   // softmax fully masked (P = 0, no rescale), which leaves O, l and m exactly
   // as skipping them would.
   auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
@@ -647,7 +656,7 @@ void attn_fwd_kernel(FwdParams p) {
       const int vc = j & 1, vp = vc ^ 1;         // V buffers of V[j] and V[j-1]
       if (G == 0) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        matrix(True{}, vbuf(vp), kbuf(b0), min(j + 2, ntiles - 1), min(j, ntiles - 1), kbuf(bm1), vbuf(vc));
+        matrix(True{}, vbuf(vp), kbuf(b0), k_tile(j + 2), v_tile(j), kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         dma_wait_barrier<Lay::ISSUES>();         // K[j+1] has landed
         softmax_phase(j);
@@ -658,7 +667,7 @@ void attn_fwd_kernel(FwdParams p) {
         prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
         barrier();
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        matrix(False{}, vbuf(vp), kbuf(b0), 0, 0, kbuf(bm1), vbuf(vc));
+        matrix(False{}, vbuf(vp), kbuf(b0), 0u, 0u, kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         barrier();
       }
@@ -671,9 +680,9 @@ void attn_fwd_kernel(FwdParams p) {
   for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
   if (grp == 0) {
 #pragma unroll
-    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, 0, 0, kbuf(0), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(0), 0u, kbuf(0), vbuf(0));
 #pragma unroll
-    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, min(1, ntiles - 1), 0, kbuf(1), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(1), 0u, kbuf(1), vbuf(0));
   }
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
