@@ -689,26 +689,41 @@ void attn_fwd_kernel(FwdParams p) {
 #endif
   if (grp == 0) run(Grp0{});
   else run(Grp1{});
-  dma_wait_all();   // the last iteration's DMAs land before the workgroup's LDS is released
+  dma_wait_all();   // the last iteration's DMAs land before the LDS is reused
 
-  // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2.  A lane holds
+  // its query row's outputs in 8-byte pieces, so storing from registers would
+  // scatter every store over 32 rows; the wave instead stages its 32 x d_v
+  // tile in LDS (rows padded by 16 bytes) and writes whole rows back, four
+  // rows of d_v = 128 per 16-byte-per-lane store.  The tiles' LDS is free once
+  // every loader's last DMAs have landed.
+  barrier();
   const float l_tot = sum_with_partner(l_part);
-  if (row_valid) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = p.o + (int64_t)(seq0 + qrow) * H * DV + (int64_t)h * DV;
+  const float inv = 1.0f / l_tot;
+  constexpr int OS = DV + 8;                       // staged row stride (elements)
+  lds_u16_t* const ost = lds + wave * kRowsPerWave * OS;
 #pragma unroll
-    for (int db = 0; db < D_BLOCKS; ++db)
+  for (int db = 0; db < D_BLOCKS; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2_t w;
-        w.x = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-        *(u32x2_t*)(op + db * 32 + 8 * jj + 4 * g) = w;
-      }
-    if (g == 0) {
-      p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2_t w;
+      w.x = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+      w.y = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+      *(__attribute__((address_space(3))) u32x2_t*)(ost + lq * OS + db * 32 + 8 * jj + 4 * g) = w;
+    }
+  {
+    constexpr int CPR = DV / 8;                      // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                    // rows per store
+    const int c = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      const u32x4_t w = *(const lds_u32x4_t*)(ost + r * OS + c * 8);
+      if (qw0 + r < L) *(u32x4_t*)(p.o + (int64_t)(seq0 + qw0 + r) * H * DV + (int64_t)h * DV + c * 8) = w;
     }
   }
+  if (row_valid && g == 0)
+    p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
 
   if (p.stats) {
     // wave totals -> one atomic per counter per wave
