@@ -101,6 +101,14 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.schedule = op.schedule;
   p.stats = reinterpret_cast<unsigned long long*>(op.stats);
 
+  p.next_stride = 0;
+  if (op.schedule == ATTN_SCHEDULE_LONGEST_FIRST) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p.next_stride = cus;
+  }
+
   const hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, np, stream);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -21,6 +21,8 @@ struct FwdParams {
   int neg_scale;              // 1: scale < 0, Q is negated on load (exact)
   float tau;                  // rescale threshold in log2 units; < 0: always rescale
   int schedule;               // 0: longest-first, 1: natural order
+  int next_stride;            // 1-D grid distance to the workgroup that starts next on the
+                              // same XCD (the CU count), whose inputs are prefetched; 0: none
   unsigned long long* stats;  // optional device counters [4]
 };
 

@@ -216,6 +216,18 @@ __device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off
 #endif
 }
 
+// One buffer_load_dword ... lds request (4 bytes per lane into the 256-byte
+// LDS block at dst), used only to pull lines into L2.
+__device__ __forceinline__ void dma_dword(const u32x4_t& rsrc, uint32_t lane_off, lds_u16_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "{m0}"(m0), "v"(lane_off), "s"(rsrc)
+               : "memory");
+#endif
+}
+
 // Buffer resource for a byte range starting at base: raw (unswizzled)
 // addressing, no stride, num_records = nbytes, so that reads at or past
 // nbytes return zeros.
@@ -308,30 +320,35 @@ void attn_fwd_kernel(FwdParams p) {
   // block longest-first within a pair: the query blocks of a pair then run
   // side by side on one XCD and share its L2 for the pair's K and V tiles.
   // Natural schedule: blockIdx = (head, sequence, query block).
-  int h, b, qblk;
-  if (p.schedule == 0) {
-    const int W = p.H * p.B * p.n_qblocks;
-    const int i = blockIdx.x, x = i % kXcds, slot = i / kXcds;
+  const int W = p.H * p.B * p.n_qblocks;
+  auto decode = [&] __device__ (int i, int& h, int& b, int& qblk) __attribute__((always_inline)) {
+    const int x = i % kXcds, slot = i / kXcds;
     const int g = x * (W / kXcds) + min(x, W % kXcds) + slot;
     const int pair = g / p.n_qblocks;
     qblk = p.n_qblocks - 1 - (g - pair * p.n_qblocks);
     h = pair / p.B;
     b = pair - h * p.B;
+  };
+  auto seq_range = [&] __device__ (int b, int& seq0, int& L) __attribute__((always_inline)) {
+    if (p.cu_seqlens) {
+      seq0 = p.cu_seqlens[b];
+      L = p.cu_seqlens[b + 1] - seq0;
+    } else {
+      seq0 = b * p.N;
+      L = p.N;
+    }
+  };
+  int h, b, qblk;
+  if (p.schedule == 0) {
+    decode(blockIdx.x, h, b, qblk);
   } else {
     h = blockIdx.x;
     b = blockIdx.y;
     qblk = blockIdx.z;
   }
-  int seq0, L, T;
-  if (p.cu_seqlens) {
-    seq0 = p.cu_seqlens[b];
-    L = p.cu_seqlens[b + 1] - seq0;
-    T = p.cu_seqlens[p.B];
-  } else {
-    seq0 = b * p.N;
-    L = p.N;
-    T = p.B * p.N;
-  }
+  int seq0, L;
+  seq_range(b, seq0, L);
+  const int T = p.cu_seqlens ? p.cu_seqlens[p.B] : p.B * p.N;
   const int q0 = qblk * kBlockM;
   if (q0 >= L) return;  // uniform over the workgroup
   const int kend = CAUSAL ? min(L, q0 + kBlockM) : L;
@@ -392,6 +409,38 @@ void attn_fwd_kernel(FwdParams p) {
   const uint32_t v_period_bytes = (uint32_t)(Lay::V_PERIOD * 64 / RV) * v_rowbytes;
   const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
   const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
+
+  // L2 prefetch for the workgroup that starts next on this XCD (workgroup
+  // blockIdx + next_stride of the 1-D grid): its Q rows and first 256 keys of
+  // K, one 128-byte line per lane, issued by group 1 near the end of the key
+  // loop.  The requests are LDS DMAs of one dword per lane into a K buffer
+  // that is no longer read, so no register waits on them; they only warm the
+  // XCD's L2 against the next workgroup's cold start.
+  u32x4_t pq_rsrc = {0u, 0u, 0u, 0u}, pk_rsrc = {0u, 0u, 0u, 0u};
+  bool prefetch_next = false;
+  if (p.schedule == 0 && p.next_stride > 0 && (int)blockIdx.x + p.next_stride < W) {
+    int h2, b2, qblk2, seq2, L2;
+    decode(blockIdx.x + p.next_stride, h2, b2, qblk2);
+    seq_range(b2, seq2, L2);
+    const int q2 = qblk2 * kBlockM;
+    if (q2 < L2) {
+      prefetch_next = true;
+      const uint32_t qrows = (uint32_t)min(kBlockM, L2 - q2), krows = (uint32_t)min(kBlockM, L2);
+      pq_rsrc = make_rsrc(p.q + (int64_t)(seq2 + q2) * qk_row + (int64_t)h2 * DQK, qrows * k_rowbytes);
+      pk_rsrc = make_rsrc(p.k + (int64_t)seq2 * qk_row + (int64_t)h2 * DQK, krows * k_rowbytes);
+    }
+  }
+  auto prefetch_l2 = [&] __device__ (lds_u16_t* garbage) __attribute__((always_inline)) {
+    constexpr int LPR = (DQK * 2 + 127) / 128;          // 128-byte lines per row
+    const int pw = wave - kWaves / 2;                   // 0..3 in group 1
+#pragma unroll
+    for (int n = 0; n < LPR; ++n) {
+      const int li = (n * 4 + pw) * 64 + lane;          // line index over 256 rows
+      const uint32_t off = (uint32_t)(li / LPR) * k_rowbytes + (uint32_t)(li % LPR) * 128u;
+      dma_dword(pq_rsrc, off, garbage);
+      dma_dword(pk_rsrc, off, garbage);
+    }
+  };
   // Byte offset of tile t in the K or V resource; a tile past the last one
   // starts at the resource's end, so its DMAs return zeros without touching
   // memory.
@@ -663,6 +712,7 @@ void attn_fwd_kernel(FwdParams p) {
         prefetch(vbuf(vc), kbuf(bp1));           // operands of matrix(j+1)
         dma_wait_barrier<Lay::K_ISSUES>();       // V[j] has landed
       } else {
+        if (prefetch_next && j == ntiles - 1) prefetch_l2(kbuf(bm1));
         softmax_phase(j - 1);
         prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
         barrier();
