@@ -208,8 +208,11 @@ __device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off
                                           lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  // s_nop: one wait state between the M0 write and its use by an LDS DMA
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // s_nop 4: five wait states.  The compiler's hazard checks do not look
+  // inside inline assembly, and a VMEM instruction may read an SGPR only five
+  // wait states after a VALU instruction wrote it (v_readlane reloads of
+  // spilled SGPRs, v_readfirstlane); an LDS DMA needs one after the M0 write.
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "{m0}"(m0), "v"(lane_off), "s"(rsrc), "s"(tile_off)
                : "memory");
@@ -221,7 +224,8 @@ __device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off
 __device__ __forceinline__ void dma_dword(const u32x4_t& rsrc, uint32_t lane_off, lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  // s_nop 4: the same wait states as dma_chunk
+  asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "{m0}"(m0), "v"(lane_off), "s"(rsrc)
                : "memory");
