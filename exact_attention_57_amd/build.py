@@ -6,9 +6,16 @@ The library is compiled ahead of time with hipcc for ``--offload-arch=gfx950``
 only.  Packed-fp32 VALU instructions are disabled for all HIP code
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
 that it does not know the feature, which is harmless.
+
+The kernels' LDS DMAs are inline assembly preceded by ``s_nop ATTN_DMA_NOP``.
+The build first compiles the kernels to assembly with one wait state
+(``ATTN_DMA_NOP=0``) and scans it (``hazards.py``); it keeps that setting only
+if no LDS DMA reads an SGPR a VALU instruction wrote fewer than five wait
+states earlier, and otherwise builds with five (``ATTN_DMA_NOP=4``).
 """
 from __future__ import annotations
 
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -40,6 +47,42 @@ def compile_flags(extra=()) -> list:
     ]
 
 
+def _hazards():
+    spec = importlib.util.spec_from_file_location("_attn_hazards", os.path.join(PKG_DIR, "hazards.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def kernel_asm(dma_nop: int, extra=(), cc: str = None) -> str:
+    """gfx950 assembly of the kernel source as build() compiles it."""
+    cc = cc or hipcc()
+    bdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    out = os.path.join(bdir, f"attn_fwd_kernel_nop{dma_nop}.s")
+    cmd = [cc, *compile_flags(extra), f"-DATTN_DMA_NOP={dma_nop}", "-x", "hip", "--cuda-device-only", "-S",
+           os.path.join(CSRC, "attn_fwd_kernel.hip"), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    with open(out) as f:
+        return f.read()
+
+
+def choose_dma_nop(extra=(), cc: str = None, verbose: bool = False) -> int:
+    """Smallest s_nop operand (0 or 4) whose compiled kernels have no LDS DMA
+    wait-state hazard; raises if even 4 leaves one."""
+    hz = _hazards()
+    problems = []
+    for nop in (0, 4):
+        n, problems = hz.scan(kernel_asm(nop, extra, cc))
+        if n == 0:
+            raise RuntimeError("no kernel with LDS DMAs found in the assembly")
+        if verbose:
+            print(f"ATTN_DMA_NOP={nop}: {n} kernels, {len(problems)} wait-state hazards", flush=True)
+        if not problems:
+            return nop
+    raise RuntimeError("LDS DMA wait-state hazard with s_nop 4: " + problems[0])
+
+
 def build(verbose: bool = False, extra=()) -> str:
     """Compile every HIP/C++ source into ``exact_attention_57_amd/libattn.so``.
 
@@ -49,10 +92,11 @@ def build(verbose: bool = False, extra=()) -> str:
     cc = hipcc()
     bdir = os.path.join(PKG_DIR, "_build")
     os.makedirs(bdir, exist_ok=True)
+    nop = choose_dma_nop(extra, cc, verbose)
     objs = []
     for src in SOURCES:
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", f"-DATTN_DMA_NOP={nop}"] if src.endswith(".hip") else []
         cmd = [cc, *compile_flags(extra), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -48,6 +48,11 @@
 
 #include "attn_fwd_kernel.h"
 
+#ifndef ATTN_DMA_NOP
+#define ATTN_DMA_NOP 4   // s_nop operand in front of each LDS DMA (4: five wait states)
+#endif
+#define ATTN_STR2(x) #x
+#define ATTN_STR(x) ATTN_STR2(x)
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 4  // matrix-phase LDS operands read ahead of their MFMA
 #endif
@@ -208,11 +213,13 @@ __device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off
                                           lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  // s_nop 4: five wait states.  The compiler's hazard checks do not look
-  // inside inline assembly, and a VMEM instruction may read an SGPR only five
-  // wait states after a VALU instruction wrote it (v_readlane reloads of
-  // spilled SGPRs, v_readfirstlane); an LDS DMA needs one after the M0 write.
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // s_nop ATTN_DMA_NOP: the compiler's hazard checks do not look inside
+  // inline assembly, and a VMEM instruction may read an SGPR only five wait
+  // states after a VALU instruction wrote it (v_readlane reloads of spilled
+  // SGPRs, v_readfirstlane); an LDS DMA needs one after the M0 write.  The
+  // default 4 (five wait states) is always safe; the build uses 0 only for a
+  // compilation whose assembly it has checked for both hazards.
+  asm volatile("s_nop " ATTN_STR(ATTN_DMA_NOP) "\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "{m0}"(m0), "v"(lane_off), "s"(rsrc), "s"(tile_off)
                : "memory");
@@ -224,8 +231,8 @@ __device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off
 __device__ __forceinline__ void dma_dword(const u32x4_t& rsrc, uint32_t lane_off, lds_u16_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  // s_nop 4: the same wait states as dma_chunk
-  asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  // the same wait states as dma_chunk
+  asm volatile("s_nop " ATTN_STR(ATTN_DMA_NOP) "\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "{m0}"(m0), "v"(lane_off), "s"(rsrc)
                : "memory");

@@ -1,123 +1,67 @@
 """Wait states in front of the kernels' LDS DMAs (CPU-only: compiles the kernel
-source to gfx950 assembly and reads it).
+source to gfx950 assembly and reads it with exact_attention_57_amd/hazards.py).
 
 The tile DMAs are inline assembly, which the compiler's hazard checks do not
-look into.  On gfx9 a VMEM instruction may read an SGPR only five wait states
-after a VALU instruction wrote it, and an LDS DMA needs one wait state after
-M0 is written.  The compiler does write such SGPRs right before a DMA when it
-reloads spilled SGPRs with v_readlane; a DMA that reads a stale buffer
-resource then addresses arbitrary memory.  This test counts the wait states
-(one per instruction, N+1 per s_nop N) between each LDS DMA and the last
-write of every SGPR it reads, in every kernel instance.
+look into: a VMEM instruction may read an SGPR only five wait states after a
+VALU instruction wrote it, and an LDS DMA needs one after M0 is written.  A
+build that reloaded a spilled buffer resource with v_readlane right before a
+DMA, one wait state ahead of it, faulted the GPU.  build() keeps one wait
+state only for assembly this check passes; these tests cover the checker and
+the always-safe setting.
 """
+import importlib.util
 import os
-import re
 import shutil
-import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "exact_attention_57_amd", "csrc", "attn_fwd_kernel.hip")
-VMEM_AFTER_VALU_SGPR = 5
-LDS_DMA_AFTER_M0 = 1
+PKG = os.path.join(ROOT, "exact_attention_57_amd")
 
 
-def _hipcc():
-    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
-        if c and os.path.exists(c):
-            return c
-    return None
+def _load(name, path):
+    spec = importlib.util.spec_from_file_location(name, path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
-@pytest.fixture(scope="module")
-def kernel_asm(tmp_path_factory):
-    hipcc = _hipcc()
-    if hipcc is None:
-        pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "k.s"
-    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", os.path.dirname(SRC),
-           "-x", "hip", "-c", SRC, "--cuda-device-only", "-S", "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
-    return out.read_text()
+hz = _load("_attn_hazards_t", os.path.join(PKG, "hazards.py"))
 
 
-def _instructions(fn_text):
-    out = []
-    for raw in fn_text.splitlines():
-        line = raw.split(";")[0].strip()
-        if not line or line.endswith(":") or line.startswith("."):
-            continue
-        out.append(line)
-    return out
+def _have_hipcc():
+    return any(c and os.path.exists(c) for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"))
 
 
-def _sgprs(operand_text):
-    regs = set()
-    for m in re.finditer(r"\bs\[(\d+):(\d+)\]", operand_text):
-        regs |= set(range(int(m.group(1)), int(m.group(2)) + 1))
-    for m in re.finditer(r"(?<![\w\[:])s(\d+)\b", operand_text):
-        regs.add(int(m.group(1)))
-    return regs
+def test_checker_flags_short_gaps():
+    bad = ["v_readlane_b32 s2, v249, 36", "s_mov_b32 m0, s9", "s_nop 0",
+           "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
+    assert hz.check_function("synthetic", bad)
+    soff = ["v_readfirstlane_b32 s5, v3", "s_mov_b32 m0, s9", "s_nop 1",
+            "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
+    assert hz.check_function("synthetic", soff)
+    m0 = ["s_mov_b32 m0, s9", "buffer_load_dword v1, s[0:3], 0 offen lds"]
+    assert hz.check_function("synthetic", m0)
+    ok = ["v_readlane_b32 s2, v249, 36", "s_mov_b32 m0, s9", "s_nop 4",
+          "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
+    assert not hz.check_function("synthetic", ok)
+    unrelated = ["v_readlane_b32 s20, v249, 36", "s_mov_b32 m0, s9", "s_nop 0",
+                 "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
+    assert not hz.check_function("synthetic", unrelated)
 
 
-def _wait_states(instrs):
-    """Wait states contributed by a run of instructions."""
-    n = 0
-    for ins in instrs:
-        m = re.match(r"s_nop\s+(\d+)", ins)
-        n += int(m.group(1)) + 1 if m else 1
-    return n
-
-
-def _check_function(name, instrs):
-    problems = []
-    for i, ins in enumerate(instrs):
-        if not (ins.startswith("buffer_load") and ins.endswith(" lds")):
-            continue
-        read = _sgprs(ins.split(None, 1)[1])
-        m0_seen = False
-        for k in range(i - 1, -1, -1):
-            between = instrs[k + 1:i]
-            gap = _wait_states(between)
-            if gap >= VMEM_AFTER_VALU_SGPR:
-                break              # nothing earlier can be too close
-            prev = instrs[k]
-            mnem, _, ops = prev.partition(" ")
-            dst = ops.split(",")[0].strip()
-            if mnem.startswith("v_") and dst.startswith("s") and _sgprs(dst) & read:
-                problems.append(f"{name}: {prev!r} -> {ins!r}: {gap} wait states")
-            if not m0_seen and dst == "m0":
-                m0_seen = True
-                if gap < LDS_DMA_AFTER_M0:
-                    problems.append(f"{name}: {prev!r} -> {ins!r}: M0 written {gap} wait states before")
-    return problems
-
-
-def test_lds_dma_wait_states(kernel_asm):
-    functions = re.split(r"\n(?=_Z\w+:)", kernel_asm)
-    checked = 0
-    problems = []
-    for fn in functions:
-        head = fn.split(":", 1)[0]
-        if "attn_fwd_kernel" not in head:
-            continue
-        body = fn.split("s_endpgm", 1)[0]
-        instrs = _instructions(body)
-        if not any(i.startswith("buffer_load") and i.endswith(" lds") for i in instrs):
-            continue
-        checked += 1
-        problems += _check_function(head, instrs)
-    assert checked >= 24, f"expected every kernel instance to contain LDS DMAs, found {checked}"
+@pytest.mark.skipif(not _have_hipcc(), reason="hipcc not available")
+def test_safe_setting_has_no_hazards():
+    build = _load("_attn_build_t", os.path.join(PKG, "build.py"))
+    n, problems = hz.scan(build.kernel_asm(4))
+    assert n >= 24, f"expected every kernel instance to contain LDS DMAs, found {n}"
     assert not problems, "\n".join(problems[:20])
 
 
-def test_checker_flags_a_short_gap():
-    """The checker itself: a v_readlane two instructions before a DMA fails."""
-    instrs = ["v_readlane_b32 s2, v249, 36", "s_mov_b32 m0, s9", "s_nop 0",
-              "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
-    assert _check_function("synthetic", instrs)
-    ok = ["v_readlane_b32 s2, v249, 36", "s_mov_b32 m0, s9", "s_nop 4",
-          "buffer_load_dwordx4 v1, s[0:3], s5 offen lds"]
-    assert not _check_function("synthetic", ok)
+@pytest.mark.skipif(not _have_hipcc(), reason="hipcc not available")
+def test_build_choice_is_hazard_free():
+    build = _load("_attn_build_t2", os.path.join(PKG, "build.py"))
+    nop = build.choose_dma_nop()
+    assert nop in (0, 4)
+    n, problems = hz.scan(build.kernel_asm(nop))
+    assert n >= 24 and not problems
