@@ -57,7 +57,7 @@
 #define ATTN_PREFETCH 4  // matrix-phase LDS operands read ahead of their MFMA
 #endif
 #ifndef ATTN_SETPRIO
-#define ATTN_SETPRIO 1  // raise the issue priority of the wave in its matrix phase
+#define ATTN_SETPRIO 1  // issue priority of the wave in its matrix phase (0: no change)
 #endif
 
 namespace attn {
@@ -715,7 +715,7 @@ void attn_fwd_kernel(FwdParams p) {
       const int bp1 = (b0 == 2) ? 0 : b0 + 1;    // (j + 1) mod 3
       const int vc = j & 1, vp = vc ^ 1;         // V buffers of V[j] and V[j-1]
       if (G == 0) {
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
         matrix(True{}, vbuf(vp), kbuf(b0), k_tile(j + 2), v_tile(j), kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         dma_wait_barrier<Lay::ISSUES>();         // K[j+1] has landed
@@ -727,7 +727,7 @@ void attn_fwd_kernel(FwdParams p) {
         softmax_phase(j - 1);
         prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
         barrier();
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
         matrix(False{}, vbuf(vp), kbuf(b0), 0u, 0u, kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         barrier();
