@@ -85,9 +85,12 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
     """Time the fp64 oracle on whole (sequence, head) pairs until the budget is spent."""
     import numpy as np
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info if p.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
     cu = inp["cu_seqlens"]
@@ -112,7 +115,18 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} of {len(pairs)} (sequence, head) pairs, fp64 NumPy/BLAS, {dt:.1f} s",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "cpu": _cpu_model(), "blas": blas, "host_cpus": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -125,6 +139,9 @@ def main():
     ap.add_argument("--poly", type=int, default=0, help="sixteenths of exps on the software exp2")
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats", action="store_true",
+                    help="after timing, run one launch with the kernel's counters and report the rescale "
+                         "skip rate and tile counts")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
@@ -220,6 +237,16 @@ def main():
                      "traffic": traffic, "kernel_ms": round(ev_ms, 4),
                      "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
     }
+    if args.stats:
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
+               scale=inp["scale"], rescale_threshold_log2=args.tau, poly_exp_sixteenths=args.poly,
+               schedule=args.schedule, stats=st, stream=stream)
+        torch.cuda.synchronize()
+        considered, taken, tiles, items = (int(x) for x in st.cpu())
+        out["stats"] = {"rescale_considered": considered, "rescale_taken": taken,
+                        "skip_rate": round(1.0 - taken / considered, 4) if considered else None,
+                        "wave_tiles": tiles, "work_items": items}
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
