@@ -521,7 +521,9 @@ void attn_fwd_kernel(FwdParams p) {
   float l_part = 0.0f;
   const float c = p.c;
   const float tau = p.tau;
-  const float tau_dec = __builtin_fmaxf(tau, 0.0f);
+  // uniform: kept in an SGPR (a VGPR copy can be spilled and reloaded)
+  const float tau_dec =
+      __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_fmaxf(tau, 0.0f))));
   uint32_t n_considered = 0, n_taken = 0, n_tiles = 0;
 
   // Row max of S^T over the tile: lane-local over its 32 keys, then with the
@@ -652,9 +654,10 @@ void attn_fwd_kernel(FwdParams p) {
     // "m_tile > m_run + max(tau, 0)".  On the first tile m_run = -inf, so
     // every lane rescales its still-zero O and l (alpha = 0).
     const bool need = m_tile > m_run + tau_dec;
+    // rescale statistics as wave totals (scalar registers)
     const bool counted = row_valid && g == 0 && t >= 1 && t <= t_last;
-    n_considered += counted ? 1u : 0u;
-    n_taken += (counted && (need || tau < 0.0f)) ? 1u : 0u;
+    n_considered += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(counted));
+    n_taken += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(counted && (need || tau < 0.0f)));
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       const float m_new = need ? __builtin_fmaxf(m_run, m_tile) : m_run;
       const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
@@ -788,10 +791,6 @@ void attn_fwd_kernel(FwdParams p) {
 
   if (p.stats) {
     // wave totals -> one atomic per counter per wave
-    for (int off = 32; off > 0; off >>= 1) {
-      n_considered += __shfl_xor(n_considered, off);
-      n_taken += __shfl_xor(n_taken, off);
-    }
     if (lane == 0) {
       atomicAdd((unsigned long long*)&p.stats[0], (unsigned long long)n_considered);
       atomicAdd((unsigned long long*)&p.stats[1], (unsigned long long)n_taken);
