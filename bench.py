@@ -2,7 +2,7 @@
 """Benchmark of the fused attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
-                    [--tau 8.0] [--poly 0] [--no-cpu-baseline]
+                    [--tau 8.0] [--poly 0] [--no-cpu-baseline] [--bwd]
 
 A step is one call of attn_fwd over the whole workload (all query blocks of
 all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
@@ -23,6 +23,12 @@ Printed (one JSON line on stdout):
 
 FLOP convention: 4*B*H*N^2*d (non-causal, d_qk = d_v = d), 2*B*H*N^2*(d_qk+d_v)
 in general, halved when causal; packed sequences sum the per-sequence counts.
+
+--bwd times the backward pass (attn_bwd: the D pass, the dK/dV kernel and the
+dQ kernel) instead, on the forward's o and lse and a seeded dO; its
+algorithmic FLOP are 2.5x the forward's (five products of the forward's
+size: S, dP, dV, dK, dQ; the kernels recompute S and dP once more, seven
+products in all).
 """
 from __future__ import annotations
 
@@ -40,6 +46,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "noncausal_b4h16n4096d128"
 KERNEL_SOURCES = ["exact_attention_57_amd/csrc/attn_fwd_kernel.hip"]
+BWD_FLOP_FACTOR = 2.5          # backward algorithmic FLOP / forward (5 products vs 2)
 
 
 def log(*a):
@@ -81,8 +88,9 @@ def load_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
-    """Time the fp64 oracle on whole (sequence, head) pairs until the budget is spent."""
+def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None) -> dict:
+    """Time the fp64 oracle on whole (sequence, head) pairs until the budget is
+    spent (the gradient oracle when ``backward_dout`` is given)."""
     import numpy as np
     import oracle
     blas = "unknown"
@@ -105,9 +113,14 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
         b, h = pairs[idx]
         s, e = int(cu[b]), int(cu[b + 1])
         sub_cu = np.array([0, e - s])
-        oracle.attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
-                         sub_cu, inp["causal"], inp["scale"])
-        done_flops += algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
+        if backward_dout is None:
+            oracle.attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
+                             sub_cu, inp["causal"], inp["scale"])
+            done_flops += algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
+        else:
+            oracle.attention_backward(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
+                                      backward_dout[s:e, h:h + 1], sub_cu, inp["causal"], inp["scale"])
+            done_flops += BWD_FLOP_FACTOR * algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -143,6 +156,7 @@ def main():
                     help="after timing, run one launch with the kernel's counters and report the rescale "
                          "skip rate and tile counts")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass (attn_bwd) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
@@ -193,6 +207,18 @@ def main():
                scale=inp["scale"], rescale_threshold_log2=args.tau,
                poly_exp_sixteenths=args.poly, schedule=args.schedule, stream=stream)
 
+    if args.bwd:
+        step()                                   # o and lse for the backward pass
+        dout_bits = workloads.make_output_grad(inp, 0)
+        dout = dev(dout_bits)
+        dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(H * inp["B"] * inp["N"], dtype=torch.float32, device="cuda")
+        flops = BWD_FLOP_FACTOR * flops
+
+        def step():                              # noqa: F811 - the backward step replaces the forward one
+            ea.bwd(q, k, v, o, lse, dout, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
+                   scale=inp["scale"], dq=dq, dk=dk, dv=dvv, delta=delta, stream=stream)
+
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -213,10 +239,10 @@ def main():
 
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
-    variant = f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
-    traffic = load_traffic(wl.key, variant)
+    variant = "bwd" if args.bwd else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
+    traffic = None if args.bwd else load_traffic(wl.key, variant)
     out = {
-        "metric": "attention fwd TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
+        "metric": ("attention bwd" if args.bwd else "attention fwd") + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -237,7 +263,11 @@ def main():
                      "traffic": traffic, "kernel_ms": round(ev_ms, 4),
                      "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
     }
-    if args.stats:
+    if args.bwd:
+        out["roofline"]["note"] = "kernel_ms spans the D pass, the dK/dV kernel and the dQ kernel"
+        # read q, k, v, o, dO, lse; write dq, dk, dv; D written and read back
+        out["roofline"]["compulsory_bytes"] = T * H * (4 * 2 * wl.d_qk + 4 * 2 * wl.d_v + 4 + 8)
+    if args.stats and not args.bwd:
         st = torch.zeros(4, dtype=torch.int64, device="cuda")
         ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
                scale=inp["scale"], rescale_threshold_log2=args.tau, poly_exp_sixteenths=args.poly,
@@ -249,7 +279,7 @@ def main():
                         "wave_tiles": tiles, "work_items": items}
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None)
     print(json.dumps(out), flush=True)
 
 

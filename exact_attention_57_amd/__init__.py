@@ -1,4 +1,4 @@
-"""Python binding of libattn.so, the MI355X fused attention forward pass.
+"""Python binding of libattn.so, the MI355X fused attention forward and backward passes.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``.  Torch is used for
@@ -15,10 +15,10 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "lib", "fwd", "fwd_raw", "debug_exp2", "strerror", "version", "geometry",
+    "AttnError", "lib", "fwd", "fwd_raw", "bwd", "bwd_raw", "debug_exp2", "strerror", "version", "geometry",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
     "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
-    "SUPPORTED_DIMS", "LIB_PATH",
+    "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "LIB_PATH",
 ]
 
 # EXACT_ATTENTION_57_AMD_LIB may point at another build of the same library
@@ -36,6 +36,7 @@ ATTN_ERR_LAUNCH = -6
 SCHEDULE_LONGEST_FIRST = 0
 SCHEDULE_NATURAL = 1
 SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
+BWD_SUPPORTED_DIMS = ((64, 64), (128, 128))
 
 
 class AttnError(RuntimeError):
@@ -86,6 +87,8 @@ def _load():
     L.attn_fwd_ex.restype = i32
     L.attn_fwd_opts_default.argtypes = [ctypes.POINTER(FwdOpts)]
     L.attn_fwd_opts_default.restype = None
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_bwd.restype = i32
     L.attn_strerror.argtypes = [i32]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_debug_exp2.argtypes = [vp, vp, i32, i32, vp]
@@ -197,6 +200,71 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
     if st != ATTN_OK:
         raise AttnError(st)
     return o, lse
+
+
+def bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr, cu_ptr,
+            B, H, N, d_qk, d_v, scale, causal, stream) -> int:
+    """Call attn_bwd with raw integer pointers; returns the status code."""
+    return int(lib.attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr, cu_ptr,
+                            int(B), int(H), int(N), int(d_qk), int(d_v), float(scale), int(bool(causal)), stream))
+
+
+def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False, scale=None,
+        dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Attention backward on torch tensors: gradients of the forward's o with
+    respect to q, k, v for the output gradient ``dout``.
+
+    Shapes and layouts as ``fwd`` (o and dout shaped like v; lse [H, T] as
+    ``fwd`` returned it); the same cu_seqlens / max_seqlen / causal / scale
+    as the forward call.  Returns (dq, dk, dv), bf16, allocated with torch
+    when not given; ``delta`` (fp32, at least H*B*N elements) is the
+    workspace for the row terms D = rowsum(dout * o).
+    """
+    import torch
+    if q.dim() == 4:
+        B, N, H, d_qk = q.shape
+        if cu_seqlens is not None:
+            raise ValueError("4-D inputs are fixed length; pass [T, H, d] with cu_seqlens")
+    elif q.dim() == 3:
+        T, H, d_qk = q.shape
+        if cu_seqlens is None:
+            N = T if max_seqlen is None else int(max_seqlen)
+            if N <= 0 or T % N:
+                raise ValueError("fixed-length [T, H, d] input needs T = B * max_seqlen")
+            B = T // N
+        else:
+            if max_seqlen is None:
+                raise ValueError("packed input needs max_seqlen")
+            B = cu_seqlens.numel() - 1
+            N = int(max_seqlen)
+    else:
+        raise ValueError("q must be [B, N, H, d] or [T, H, d]")
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or o.shape != v.shape or dout.shape != v.shape:
+        raise ValueError("q, k, v, o, dout shapes disagree")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 CUDA tensor")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device) if dv is None else dv
+    if delta is None:
+        delta = torch.empty(H * B * N, dtype=torch.float32, device=q.device)
+    elif delta.dtype != torch.float32 or delta.numel() < H * B * N or not delta.is_cuda:
+        raise ValueError("delta must be an fp32 CUDA tensor of at least H*B*N elements")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    st = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                 cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def debug_exp2(x, use_poly: bool, y=None, stream=None):

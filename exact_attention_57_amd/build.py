@@ -28,7 +28,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["attn_fwd_kernel.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 
 

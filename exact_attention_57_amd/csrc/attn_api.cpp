@@ -6,11 +6,12 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "attn_bwd_kernel.h"
 #include "attn_fwd_kernel.h"
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -117,6 +118,47 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream) {
   return attn_fwd_ex(q, k, v, o, lse, cu_seqlens, B, H, N, d_qk, d_v, scale, causal, stream, nullptr);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+             float scale, int causal, hipStream_t stream) {
+  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
+  if (!((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (N == 0) return ATTN_OK;  // no tokens: nothing to do
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(delta, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return ATTN_ERR_ALIGN;
+  const int rows = attn_grad::block_rows();
+  const int64_t nb = ((int64_t)N + rows - 1) / rows;
+  if ((int64_t)H * B * nb > INT32_MAX) return ATTN_ERR_SHAPE;   // one workgroup per (sequence, head, block)
+  if ((int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;        // token indices are 32-bit in the kernels
+  if ((int64_t)B * N * H > INT32_MAX) return ATTN_ERR_SHAPE;    // rows of the D pass
+
+  attn_grad::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.delta = delta;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_blocks = (int)nb;
+  p.scale = scale;
+  p.c = scale * 1.44269504088896340736f;
+  const hipError_t err = attn_grad::launch_bwd(p, d_qk, d_v, causal != 0, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t stream) {

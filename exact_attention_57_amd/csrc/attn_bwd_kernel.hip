@@ -1,0 +1,479 @@
+// Exact-attention backward kernels for gfx950 (CDNA4, MI355X).
+//
+// What they compute: the gradients of O = softmax(scale Q K^T [+ causal mask]) V
+// with respect to Q, K and V, given dO and the forward pass's O and LSE --
+// the backward pass of the FlashAttention-4 pages (wittx, section on
+// backward-pass optimisation; newton wiki, core-technology section): per
+// (sequence, head), with P recomputed from the stored LSE,
+//
+//   D_i   = dO_i . O_i                      (row term of the softmax Jacobian)
+//   P_ij  = exp(scale q_i.k_j - LSE_i)      (= 2^(c s_ij - LSE_i log2 e), c = scale log2 e)
+//   dV    = P^T dO        dP = dO V^T       dS = P * (dP - D)
+//   dQ    = scale dS K    dK = scale dS^T Q
+//
+// The pages' design reduces dQ over the key sequence with global atomic adds
+// (halved there by pairing two thread blocks) and offers a deterministic
+// mode that serialises those reductions.  Here no step reduces across
+// workgroups: one kernel owns a block of 128 keys and accumulates its dK and
+// dV over every query tile that sees those keys; a second owns a block of
+// 128 queries and accumulates its dQ over the key tiles.  Each recomputes the
+// score and dP tiles it needs (7 matrix products instead of 5), and the
+// results are bitwise reproducible run to run.
+//
+// Layout of the work on the chip: a workgroup is 4 wave64s, one per SIMD,
+// each owning 32 rows of its block; a 64-row tile of the streamed operands
+// (Q and dO for dK/dV, K and V for dQ) is staged in LDS once per workgroup
+// and read by all four waves, while the next tile's global loads are in
+// flight.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators:
+//   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
+//               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
+//   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V in registers)
+//               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read)
+// With the streamed tile's rows read in an order with bits 2 and 3 of the
+// row index swapped, accumulator registers 0..7 and 8..15 of a 32 x 32
+// block hold 8 consecutive rows -- the B-operand slots of the next product --
+// so P and dS go from the accumulators to bf16 B operands in registers.  A
+// tile read both row-wise and transposed is stored twice, once in each
+// swizzled layout, so both reads are free of bank conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_bwd_kernel.h"
+
+namespace attn_grad {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;                     // one per SIMD
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRows = 32;                     // block rows per wave
+constexpr int kBlock = kRows * kWaves;        // block rows per workgroup
+constexpr int kTile = 64;                     // streamed rows per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+int block_rows() { return kBlock; }
+
+// LDS layouts of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
+// bytes): chunk c of row r sits at position c ^ f(r).
+//  * row layout, read 16 bytes per lane with 16 consecutive rows per
+//    quarter-wave: f(r) = r mod 16 (R = 16), (r/2) mod 8 (R = 8);
+//  * transposed layout, read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
+//    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8).
+// Both are invariant under a shift of r by a multiple of 16.
+template <int D>
+struct RowSwz {
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  __device__ static int f(int r) { return (D == 128) ? (r & 15) : ((r >> 1) & 7); }
+};
+template <int D>
+struct TrSwz {
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  __device__ static int f(int r) { return (D == 128) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+// Two fp32 values -> two bf16 (round to nearest even) in one dword, low first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ int total_tokens(const BwdParams& p) {
+  return p.cu_seqlens ? p.cu_seqlens[p.B] : p.B * p.N;
+}
+__device__ __forceinline__ void seq_range(const BwdParams& p, int b, int& seq0, int& L) {
+  if (p.cu_seqlens) {
+    seq0 = p.cu_seqlens[b];
+    L = p.cu_seqlens[b + 1] - seq0;
+  } else {
+    seq0 = b * p.N;
+    L = p.N;
+  }
+}
+
+// Row sigma(m): m with bits 2 and 3 swapped.
+__device__ __forceinline__ int sigma(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// ---- D = rowsum(dO * O) over d_v, one row (t, h) per DV/8 lanes.
+template <int DV>
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = DV / 8;                 // lanes per row, 16 bytes each
+  constexpr int RPB = kThreads / LPR;         // rows per workgroup
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // row = t H + h
+  const int c = threadIdx.x % LPR;
+  const int T = total_tokens(p);
+  const int64_t nrows = (int64_t)T * p.H;
+  float acc = 0.0f;
+  if (row < nrows) {
+    const u32x4_t a = *(const u32x4_t*)(p.o + row * DV + c * 8);
+    const u32x4_t d = *(const u32x4_t*)(p.dout + row * DV + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(d[i]) + bf16_hi(a[i]) * bf16_hi(d[i]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < nrows && c == 0) {
+    const int t = (int)(row / p.H), h = (int)(row % p.H);
+    p.delta[(int64_t)h * T + t] = acc;
+  }
+}
+
+// ---- tiles: global -> registers (rows past L read as zeros) -> LDS.
+template <int D>
+struct TileRegs {
+  static constexpr int N = kTile * D / 8 / kThreads;
+  u32x4_t c[N];
+};
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D>& t, const uint16_t* base, int64_t row_stride, int row0, int L,
+                                          int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::N; ++i) {
+    const int idx = i * kThreads + tid, r = idx / CPR, ch = idx % CPR;
+    const int row = row0 + r;
+    t.c[i] = (row < L) ? *(const u32x4_t*)(base + (int64_t)row * row_stride + ch * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+template <int D, bool ROW, bool TR>
+__device__ __forceinline__ void tile_store(const TileRegs<D>& t, lds_u16_t* row_l, lds_u16_t* tr_l, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::N; ++i) {
+    const int idx = i * kThreads + tid, r = idx / CPR, ch = idx % CPR;
+    if (ROW) *(lds_u32x4_t*)(row_l + r * D + ((ch ^ RowSwz<D>::f(r)) * 8)) = t.c[i];
+    if (TR) *(lds_u32x4_t*)(tr_l + r * D + ((ch ^ TrSwz<D>::f(r)) * 8)) = t.c[i];
+  }
+}
+
+// Per-lane LDS element offsets.  Row reads (A operand, 32 rows in sigma order,
+// k-step s: 8 columns from 16 s + 8 g); transposed reads (A operand: columns
+// db*32 + (lane % 32) at 8 consecutive rows from 8 g, as two 4-row reads).
+template <int D>
+struct Reads {
+  int row[D / 16];
+  int tr[D / 32];
+  __device__ Reads(int lane) {
+    const int g = lane / 32, sig = sigma(lane % 32);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) row[s] = sig * D + (((2 * s + g) ^ RowSwz<D>::f(sig)) * 8);
+    // in each group of 16 lanes, lane s reads 4 consecutive columns of row
+    // s/4 (+ 8 for the upper lane groups); the transpose hands lane i the
+    // values of 4 consecutive rows at column i
+    const int lg = lane / 16, sl = lane % 16, vrow = 8 * (lg / 2) + sl / 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + 16 * (lg % 2) + 4 * (sl % 4);
+      tr[db] = vrow * D + (((d / 8) ^ TrSwz<D>::f(vrow)) * 8) + (d % 8);
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ bf16x8_t read_row(const lds_u16_t* tile, const Reads<D>& rd, int s, int blk) {
+  return *(const lds_bf16x8_t*)(tile + rd.row[s] + blk * 32 * D);
+}
+// rows r0 .. r0+15 (r0 a multiple of 16), column block db
+template <int D>
+__device__ __forceinline__ bf16x8_t read_tr(const lds_u16_t* tile, const Reads<D>& rd, int db, int r0) {
+  const lds_u16_t* a = tile + rd.tr[db] + r0 * D;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * D));
+  const i16x4_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+}
+
+// 8 bf16 at row `row` of a [.., H, D] tensor, columns 16 s + 8 g (zeros if !ok)
+template <int D>
+__device__ __forceinline__ void load_b_operand(bf16x8_t (&reg)[D / 16], const uint16_t* t, int64_t row, int H, int h,
+                                               int g, bool ok) {
+  const uint16_t* ptr = t + row * (int64_t)H * D + (int64_t)h * D + 8 * g;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u32x4_t raw = ok ? *(const u32x4_t*)(ptr + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+    reg[s] = __builtin_bit_cast(bf16x8_t, raw);
+  }
+}
+
+// Stage a wave's 32 x D transposed accumulator blocks (column = lane % 32 =
+// output row, register r of block db = column db*32 + 8(r/4) + 4g + r%4)
+// times `mul` as bf16 rows in LDS (row stride D + 8), then store whole rows
+// to out[(row0 + r), h, :] for r < nvalid.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float mul, lds_u16_t* stage, uint16_t* out,
+                                           int64_t row0, int nvalid, int H, int h, int lane) {
+  constexpr int OS = D + 8;
+  const int g = lane / 32, lq = lane % 32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2_t w;
+      w.x = pack_bf16x2(acc[db][4 * jj + 0] * mul, acc[db][4 * jj + 1] * mul);
+      w.y = pack_bf16x2(acc[db][4 * jj + 2] * mul, acc[db][4 * jj + 3] * mul);
+      *(lds_u32x2_t*)(stage + lq * OS + db * 32 + 8 * jj + 4 * g) = w;
+    }
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;           // rows per store
+  const int c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < kRows / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const u32x4_t w = *(const lds_u32x4_t*)(stage + r * OS + c * 8);
+    if (r < nvalid) *(u32x4_t*)(out + (row0 + r) * (int64_t)H * D + (int64_t)h * D + c * 8) = w;
+  }
+}
+
+// ---- dQ: one workgroup per block of 128 query rows of one (sequence, head).
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
+  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
+  constexpr int TILE_ELEMS = 2 * K_ELEMS + V_ELEMS;
+  constexpr int STAGE_ELEMS = kWaves * kRows * (DQK + 8);
+  constexpr int LDS_ELEMS = TILE_ELEMS > STAGE_ELEMS ? TILE_ELEMS : STAGE_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+  lds_u16_t* const k_row = lds;
+  lds_u16_t* const k_tr = lds + K_ELEMS;
+  lds_u16_t* const v_row = lds + 2 * K_ELEMS;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  const int blk = blockIdx.x % p.n_blocks, bh = blockIdx.x / p.n_blocks;
+  const int h = bh % p.H, b = bh / p.H;
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int q0 = blk * kBlock;
+  if (q0 >= L) return;
+  const int qw0 = q0 + wave * kRows;
+  const int qrow = qw0 + lq;
+  const bool row_valid = qrow < L;
+
+  bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
+  load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
+  load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
+  const int T = total_tokens(p);
+  const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
+  const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
+
+  const Reads<DQK> rk(lane);
+  const Reads<DV> rv(lane);
+  const int kend = CAUSAL ? min(L, q0 + kBlock) : L;
+  const int ntiles = (kend + kTile - 1) / kTile;
+  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
+  const uint16_t* const kbase = p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK;
+  const uint16_t* const vbase = p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV;
+
+  f32x16_t dqacc[QBLK];
+#pragma unroll
+  for (int i = 0; i < QBLK; ++i) dqacc[i] = f32x16_t{};
+  const f32x16_t zero = {};
+
+  TileRegs<DQK> kr;
+  TileRegs<DV> vr;
+  tile_load<DQK>(kr, kbase, qk_stride, 0, L, tid);
+  tile_load<DV>(vr, vbase, v_stride, 0, L, tid);
+  for (int t = 0; t < ntiles; ++t) {
+    tile_store<DQK, true, true>(kr, k_row, k_tr, tid);
+    tile_store<DV, true, false>(vr, v_row, v_row, tid);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      tile_load<DQK>(kr, kbase, qk_stride, (t + 1) * kTile, L, tid);
+      tile_load<DV>(vr, vbase, v_stride, (t + 1) * kTile, L, tid);
+    }
+    const int k0 = t * kTile;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16_t s = zero, dp = zero;
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DQK>(k_row, rk, ks, kb), qreg[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DV>(v_row, rv, vs, kb), doreg[vs], dp, 0, 0, 0);
+      // dS^T for this lane's query and keys k0 + kb*32 + 16(r/8) + 8g + r%8
+      uint32_t dsb[2][4];
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+        const bool ok = row_valid && key < L && (!CAUSAL || key <= qrow);
+        const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) : 0.0f;
+        ds[r] = pv * (dp[r] - dq_row);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dsb[hh][jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
+#pragma unroll
+        for (int db = 0; db < QBLK; ++db)
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh), bop,
+                                                              dqacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
+}
+
+// ---- dK, dV: one workgroup per block of 128 key rows of one (sequence, head).
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, KBLK = DQK / 32, VBLK = DV / 32, QB = kTile / 32;
+  constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
+  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;   // + lse, D (fp32)
+  constexpr int STAGE_ELEMS = kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
+  constexpr int LDS_ELEMS = TILE_ELEMS > STAGE_ELEMS ? TILE_ELEMS : STAGE_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+  lds_u16_t* const q_row = lds;
+  lds_u16_t* const q_tr = lds + Q_ELEMS;
+  lds_u16_t* const do_row = lds + 2 * Q_ELEMS;
+  lds_u16_t* const do_tr = lds + 2 * Q_ELEMS + O_ELEMS;
+  lds_f32_t* const lse_s = (lds_f32_t*)(lds + 2 * Q_ELEMS + 2 * O_ELEMS);
+  lds_f32_t* const d_s = lse_s + kTile;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  const int blk = blockIdx.x % p.n_blocks, bh = blockIdx.x / p.n_blocks;
+  const int h = bh % p.H, b = bh / p.H;
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int k0 = blk * kBlock;
+  if (k0 >= L) return;
+  const int kw0 = k0 + wave * kRows;
+  const int key = kw0 + lq;
+  const bool key_valid = key < L;
+
+  bf16x8_t kreg[QK_STEPS], vreg[V_STEPS];
+  load_b_operand<DQK>(kreg, p.k, seq0 + key, p.H, h, g, key_valid);
+  load_b_operand<DV>(vreg, p.v, seq0 + key, p.H, h, g, key_valid);
+
+  const Reads<DQK> rq(lane);
+  const Reads<DV> ro(lane);
+  const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
+  const int ntiles = (L - qstart + kTile - 1) / kTile;
+  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
+  const uint16_t* const qbase = p.q + (int64_t)seq0 * qk_stride + (int64_t)h * DQK;
+  const uint16_t* const dobase = p.dout + (int64_t)seq0 * v_stride + (int64_t)h * DV;
+  const int T = total_tokens(p);
+  const float* const lse_h = p.lse + (int64_t)h * T + seq0;
+  const float* const d_h = p.delta + (int64_t)h * T + seq0;
+
+  f32x16_t dkacc[KBLK], dvacc[VBLK];
+#pragma unroll
+  for (int i = 0; i < KBLK; ++i) dkacc[i] = f32x16_t{};
+#pragma unroll
+  for (int i = 0; i < VBLK; ++i) dvacc[i] = f32x16_t{};
+  const f32x16_t zero = {};
+
+  TileRegs<DQK> qr;
+  TileRegs<DV> dr;
+  float rowval = 0.0f;                      // threads 0..63: LSE (log2 units); 64..127: D
+  auto load_tile = [&] __device__ (int q0t) __attribute__((always_inline)) {
+    tile_load<DQK>(qr, qbase, qk_stride, q0t, L, tid);
+    tile_load<DV>(dr, dobase, v_stride, q0t, L, tid);
+    const int r = q0t + (tid % kTile);
+    if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] * kLog2e : d_h[r]) : 0.0f;
+  };
+  load_tile(qstart);
+  for (int t = 0; t < ntiles; ++t) {
+    tile_store<DQK, true, true>(qr, q_row, q_tr, tid);
+    tile_store<DV, true, true>(dr, do_row, do_tr, tid);
+    if (tid < 2 * kTile) lse_s[tid] = rowval;      // lse_s and d_s are adjacent
+    __syncthreads();
+    const int q0t = qstart + t * kTile;
+    if (t + 1 < ntiles) load_tile(q0t + kTile);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16_t s = zero, dp = zero;
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DQK>(q_row, rq, ks, qb), kreg[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DV>(do_row, ro, vs, qb), vreg[vs], dp, 0, 0, 0);
+      // P and dS for this lane's key and queries q0t + qb*32 + 16(r/8) + 8g + r%8
+      uint32_t pb[2][4], dsb[2][4];
+      float pv[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+        const int query = q0t + qi;
+        const bool ok = key_valid && query < L && (!CAUSAL || key <= query);
+        pv[r] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse_s[qi])) : 0.0f;
+        ds[r] = pv[r] * (dp[r] - d_s[qi]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          pb[hh][jj] = pack_bf16x2(pv[8 * hh + 2 * jj], pv[8 * hh + 2 * jj + 1]);
+          dsb[hh][jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
+        }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pb[hh]);
+        const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
+#pragma unroll
+        for (int db = 0; db < VBLK; ++db)
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DV>(do_tr, ro, db, qb * 32 + 16 * hh), pop,
+                                                              dvacc[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < KBLK; ++db)
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DQK>(q_tr, rq, db, qb * 32 + 16 * hh), dsop,
+                                                              dkacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
+  store_rows<DQK>(dkacc, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+  store_rows<DV>(dvacc, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+}
+
+template <int DQK, int DV>
+hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.N * p.H;   // at least T*H; the kernel stops at T*H
+  constexpr int RPB = kThreads / (DV / 8);
+  hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, s, p);
+  const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
+  if (causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return launch_dims<64, 64>(p, causal, s);
+  if (d_qk == 128 && d_v == 128) return launch_dims<128, 128>(p, causal, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn_grad

@@ -134,6 +134,34 @@ int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t s
  * ATTN_ERR_UNSUPPORTED for an unsupported (d_qk, d_v).  No HIP call. */
 int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile, int* rows_per_wave);
 
+/* Backward pass: gradients of the forward's O with respect to q, k and v.
+ *
+ * The backward pass of the same pages (wittx news "FlashAttention-4",
+ * section on backward-pass optimisation; newton.com.tw wiki, core-technology
+ * section): given dO = dLoss/dO and the forward's o and lse, with P the
+ * softmax probabilities recomputed from lse,
+ *     D_i = dO_i . O_i,   dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *     dv_j = sum_i P_ij dO_i          (j over the keys query i sees).
+ * dq is reduced over the keys inside one workgroup per query block and dk,
+ * dv inside one per key block: no atomics, the result is the same bit for bit
+ * on every run (the pages' deterministic mode, here the only mode).
+ *
+ * Layouts as for attn_fwd: q, k, dq, dk bf16 [T, H, d_qk]; v, o, dout, dv
+ * bf16 [T, H, d_v]; lse fp32 [H, T] as attn_fwd wrote it (natural log).
+ * delta: caller-owned fp32 workspace [H, T] (T = B*N for fixed length, or
+ * cu_seqlens[B]; H*B*N floats always suffice), overwritten with D; its
+ * contents on entry are ignored.  dq, dk, dv are overwritten.  cu_seqlens,
+ * B, H, N, scale and causal must be the values of the forward call.
+ * Supported (d_qk, d_v): (64, 64), (128, 128); (192, 128) returns
+ * ATTN_ERR_UNSUPPORTED.  Alignment: 16 bytes for the bf16 tensors, 4 for
+ * lse, delta and cu_seqlens.  Ownership, streams and errors as attn_fwd
+ * (validation before any HIP call, asynchronous on `stream`). */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+             float scale, int causal, hipStream_t stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int attn_version(void);
 

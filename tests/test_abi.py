@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("attn_fwd", "attn_fwd_ex", "attn_fwd_opts_default", "attn_strerror",
-                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry"):
+                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry", "attn_bwd"):
         assert want in names
 
 
@@ -122,3 +122,35 @@ def test_geometry_query():
         assert g["keys_per_tile"] % 32 == 0
     with pytest.raises(ea.AttnError):
         ea.geometry(96, 96)
+
+
+def call_bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, delta=P, cu=None, B=1, H=1, N=1,
+                d_qk=128, d_v=128, scale=1.0, causal=0, stream=None)
+    args.update(kw)
+    return ea.bwd_raw(args["q"], args["k"], args["v"], args["o"], args["do"], args["lse"], args["dq"],
+                      args["dk"], args["dv"], args["delta"], args["cu"], args["B"], args["H"], args["N"],
+                      args["d_qk"], args["d_v"], args["scale"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), ea.ATTN_ERR_SHAPE),
+    (dict(H=0), ea.ATTN_ERR_SHAPE),
+    (dict(N=-1), ea.ATTN_ERR_SHAPE),
+    (dict(B=2, N=2 ** 30 + 1), ea.ATTN_ERR_SHAPE),
+    (dict(d_qk=192, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), ea.ATTN_ERR_VALUE),
+    (dict(do=None), ea.ATTN_ERR_NULL),
+    (dict(delta=None), ea.ATTN_ERR_NULL),
+    (dict(dv=None), ea.ATTN_ERR_NULL),
+    (dict(o=P + 8), ea.ATTN_ERR_ALIGN),
+    (dict(dk=P + 2), ea.ATTN_ERR_ALIGN),
+    (dict(delta=P + 2), ea.ATTN_ERR_ALIGN),
+    (dict(cu=P + 1), ea.ATTN_ERR_ALIGN),
+    (dict(N=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, delta=None),
+     ea.ATTN_OK),
+])
+def test_bwd_validation_codes(kw, code):
+    assert call_bwd(**kw) == code
+

@@ -1,0 +1,152 @@
+"""GPU parity of the backward pass (attn_bwd) against the fp64 gradient oracle.
+
+Tolerances, per gradient tensor G in {dq, dk, dv} (bf16 inputs, fp32
+accumulation, bf16 outputs):
+  relative RMS  ||G_gpu - G_ref||_2 / ||G_ref||_2  <= 1e-2
+  max abs       max |G_gpu - G_ref|               <= 2e-2 * max |G_ref|
+Derivation: rounding the outputs to bf16 alone gives a relative RMS of about
+2^-9 / sqrt(3) = 0.11 %; P and dS are rounded to bf16 before the second
+products (about 2^-9 relative per term, independent across terms), and D =
+dO.O uses the forward's bf16 output (relative error about 2^-9 in O), which
+moves dS by P * dD.  Together these stay a few tenths of a percent; the
+bounds leave a margin of about 3-10x, and a wrong mask, scale, transpose or
+sign gives errors of order 100 %.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _gpu import say, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL_RMS = 1e-2
+TOL_MAX_REL = 2e-2
+
+
+def gpu_fwd_bwd(inp, causal, scale, dout_bits, packed):
+    torch = torch_cuda()
+    import exact_attention_57_amd as ea
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    do = to_dev(dout_bits)
+    cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], dtype=np.int32)).cuda() if packed else None
+    N = max(int(inp["N"]), 1)
+    o, lse = ea.fwd(q, k, v, cu_seqlens=cu, max_seqlen=N, causal=causal, scale=scale)
+    dq, dk, dv = ea.bwd(q, k, v, o, lse, do, cu_seqlens=cu, max_seqlen=N, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def f64(t, heads=None):
+    a = t.float().cpu().numpy().astype(np.float64)
+    return a if heads is None else a[:, heads]
+
+
+def check(name, got, ref):
+    err = got - ref
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(err)) / max(nref, 1e-30)
+    mx = float(np.max(np.abs(err))) if err.size else 0.0
+    mref = float(np.max(np.abs(ref))) if ref.size else 0.0
+    say(f"  {name}: rel_rms {rel:.3e}  max_abs {mx:.3e}  (max |ref| {mref:.3e})")
+    if nref == 0.0:
+        assert mx == 0.0, name
+        return
+    assert rel <= TOL_REL_RMS, name
+    assert mx <= TOL_MAX_REL * mref, name
+
+
+def full_check(inp, causal, scale, what, packed=None, seed=0):
+    lengths = np.asarray(inp["lengths"])
+    if packed is None:
+        packed = bool(len(lengths) == 0 or lengths.min() != lengths.max())
+    inp = dict(inp)
+    dout = workloads.make_output_grad(inp, seed)
+    say(f"[bwd parity] {what}: lengths {list(lengths)[:8]} H={inp['H']} d=({inp['d_qk']},{inp['d_v']}) "
+        f"causal={causal} packed={packed}")
+    dq, dk, dv = gpu_fwd_bwd(inp, causal, scale, dout, packed)
+    rq, rk, rv, _ = oracle.attention_backward(inp["q"], inp["k"], inp["v"], dout, inp["cu_seqlens"],
+                                              causal, scale)
+    check("dq", f64(dq), rq)
+    check("dk", f64(dk), rk)
+    check("dv", f64(dv), rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_workload_all_elements(causal):
+    inp = workloads.make_custom_inputs([256], 2, 64, 64, seed=0)
+    full_check(inp, causal, 0.125, "B1 H2 N256 d64")
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_packed_all_elements(dims, causal):
+    inp = workloads.make_custom_inputs([1, 77, 300, 129], 2, dims[0], dims[1], seed=3)
+    full_check(inp, causal, 1.0 / np.sqrt(dims[0]), f"packed ragged d{dims}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fixed_length_ragged_tail(causal):
+    inp = workloads.make_custom_inputs([300, 300], 2, 128, 128, seed=5)
+    full_check(inp, causal, 1.0 / np.sqrt(128), "fixed N300 d128", packed=False)
+
+
+def test_empty_and_single_token_sequences():
+    inp = workloads.make_custom_inputs([0, 1, 0, 64, 5], 3, 64, 64, seed=7)
+    full_check(inp, True, 0.125, "empty and single-token sequences", packed=True)
+
+
+def test_large_logits_and_negative_scale():
+    inp = workloads.make_custom_inputs([200, 130], 2, 128, 128, seed=11, std=3.0)
+    full_check(inp, True, 0.3, "std 3 inputs, scale 0.3 (large logits)", packed=True)
+    full_check(inp, False, -0.05, "negative scale", packed=True)
+
+
+def test_deterministic():
+    """No atomics: two runs give the same bits."""
+    torch = torch_cuda()
+    inp = workloads.make_custom_inputs([700, 333], 4, 128, 128, seed=13)
+    dout = workloads.make_output_grad(inp, 1)
+    a = gpu_fwd_bwd(inp, True, 0.088, dout, True)
+    b = gpu_fwd_bwd(inp, True, 0.088, dout, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_column_sum_identities_mid_size():
+    """sum_j dk_j = 0 and sum_j dv_j = sum_i dO_i per (sequence, head), at a
+    size where the full oracle would be slow to compare element by element."""
+    inp = workloads.make_custom_inputs([2048, 1500], 4, 128, 128, seed=17)
+    dout = workloads.make_output_grad(inp, 2)
+    dq, dk, dv = gpu_fwd_bwd(inp, True, 1.0 / np.sqrt(128), dout, True)
+    dk, dv = f64(dk), f64(dv)
+    do = workloads.bf16_bits_to_f32(dout).astype(np.float64)
+    cu = inp["cu_seqlens"]
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        sk = np.abs(dk[s:e].sum(axis=0)) / np.abs(dk[s:e]).sum(axis=0)
+        sv = np.abs(dv[s:e].sum(axis=0) - do[s:e].sum(axis=0)) / np.abs(dv[s:e]).sum(axis=0)
+        say(f"  seq {b}: max |sum dk| / sum |dk| = {sk.max():.2e}, max |sum dv - sum dO| / sum |dv| = {sv.max():.2e}")
+        assert sk.max() <= 1e-2 and sv.max() <= 1e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_size_sampled_heads(causal):
+    """At the benchmark shape (B4 H16 N4096 d128), whole (sequence, head) pairs
+    of the last sequence against the oracle, with and without the causal mask."""
+    wl = workloads.workload("noncausal_b4h16n4096d128")
+    inp = workloads.make_inputs(wl, seed=0)
+    dout = workloads.make_output_grad(inp, 0)
+    say(f"[bwd parity] full size {wl.key} causal={causal}")
+    dq, dk, dv = gpu_fwd_bwd(inp, causal, inp["scale"], dout, False)
+    heads = [0, inp["H"] - 1]
+    cu = inp["cu_seqlens"]
+    b = inp["B"] - 1
+    s, e = int(cu[b]), int(cu[b + 1])
+    one = np.array([0, e - s], dtype=np.int64)
+    rq, rk, rv, _ = oracle.attention_backward(inp["q"][s:e], inp["k"][s:e], inp["v"][s:e], dout[s:e], one,
+                                              causal, inp["scale"], heads=heads)
+    check("dq", f64(dq[s:e], heads), rq)
+    check("dk", f64(dk[s:e], heads), rk)
+    check("dv", f64(dv[s:e], heads), rv)

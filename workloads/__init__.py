@@ -29,6 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
+    "make_output_grad",
     "Workload",
     "WORKLOADS",
     "workload",
@@ -241,3 +242,10 @@ def make_custom_inputs(lengths, H: int, d_qk: int, d_v: int, seed: int = 0,
     return dict(q=q, k=k, v=v, cu_seqlens=cu.astype(np.int32), lengths=lengths,
                 B=len(lengths), H=H, N=int(lengths.max()) if len(lengths) else 0,
                 d_qk=d_qk, d_v=d_v, T=T)
+
+
+def make_output_grad(inp: dict, seed: int = 0) -> np.ndarray:
+    """Seeded N(0, 1) bf16 output gradient dO [T, H, d_v] for an input dict
+    (its own random stream, independent of q, k, v)."""
+    return _normal_bf16(seed, 3, (int(inp["T"]), int(inp["H"]), int(inp["d_v"])))
+
