@@ -299,25 +299,49 @@ void bwd_dq_kernel(BwdParams p) {
       tile_load<DV>(vr, vbase, v_stride, (t + 1) * kTile, L, tid);
     }
     const int k0 = t * kTile;
+    // masks only where the tile reaches past the sequence end or the
+    // wave's diagonal, or the wave has rows past the end
+    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      // every LDS operand of the score and dP products is requested before
+      // the first of them, so the MFMAs queue behind the reads instead of
+      // each waiting out a read's latency
+      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS], a_q[2][QBLK];
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(k_row, rk, ks, kb);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16_t s = zero, dp = zero;
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DQK>(k_row, rk, ks, kb), qreg[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], qreg[ks], s, 0, 0, 0);
 #pragma unroll
       for (int vs = 0; vs < V_STEPS; ++vs)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DV>(v_row, rv, vs, kb), doreg[vs], dp, 0, 0, 0);
-      // dS^T for this lane's query and keys k0 + kb*32 + 16(r/8) + 8g + r%8
-      uint32_t dsb[2][4];
-      float ds[16];
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
+      // K^T operands of the dQ product: requested now, they land while the
+      // exponentials run
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-        const bool ok = row_valid && key < L && (!CAUSAL || key <= qrow);
-        const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) : 0.0f;
-        ds[r] = pv * (dp[r] - dq_row);
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < QBLK; ++db) a_q[hh][db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
+      __builtin_amdgcn_sched_barrier(0);
+      // dS^T for this lane's query and keys k0 + kb*32 + 16(r/8) + 8g + r%8
+      float ds[16];
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+          const bool ok = row_valid && key < L && (!CAUSAL || key <= qrow);
+          const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) : 0.0f;
+          ds[r] = pv * (dp[r] - dq_row);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) * (dp[r] - dq_row);
       }
+      uint32_t dsb[2][4];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -327,8 +351,7 @@ void bwd_dq_kernel(BwdParams p) {
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
 #pragma unroll
         for (int db = 0; db < QBLK; ++db)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh), bop,
-                                                              dqacc[db], 0, 0, 0);
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[hh][db], bop, dqacc[db], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -406,26 +429,43 @@ void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     const int q0t = qstart + t * kTile;
     if (t + 1 < ntiles) load_tile(q0t + kTile);
+    const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // all LDS operands of the score and dP products first (see the dQ kernel)
+      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS], a_v[2][VBLK], a_k[2][KBLK];
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(q_row, rq, ks, qb);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(do_row, ro, vs, qb);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16_t s = zero, dp = zero;
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DQK>(q_row, rq, ks, qb), kreg[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], kreg[ks], s, 0, 0, 0);
 #pragma unroll
       for (int vs = 0; vs < V_STEPS; ++vs)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<DV>(do_row, ro, vs, qb), vreg[vs], dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], vreg[vs], dp, 0, 0, 0);
+      // dO^T operands of the dV product, landing while P and dS are computed
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < VBLK; ++db) a_v[hh][db] = read_tr<DV>(do_tr, ro, db, qb * 32 + 16 * hh);
+      __builtin_amdgcn_sched_barrier(0);
       // P and dS for this lane's key and queries q0t + qb*32 + 16(r/8) + 8g + r%8
-      uint32_t pb[2][4], dsb[2][4];
       float pv[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-        const int query = q0t + qi;
-        const bool ok = key_valid && query < L && (!CAUSAL || key <= query);
-        pv[r] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse_s[qi])) : 0.0f;
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse_s[qi]));
+        if (masked) {
+          const int query = q0t + qi;
+          pv[r] = (key_valid && query < L && (!CAUSAL || key <= query)) ? e : 0.0f;
+        } else {
+          pv[r] = e;
+        }
         ds[r] = pv[r] * (dp[r] - d_s[qi]);
       }
+      uint32_t pb[2][4], dsb[2][4];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -436,15 +476,21 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pb[hh]);
-        const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
 #pragma unroll
         for (int db = 0; db < VBLK; ++db)
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DV>(do_tr, ro, db, qb * 32 + 16 * hh), pop,
-                                                              dvacc[db], 0, 0, 0);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[hh][db], pop, dvacc[db], 0, 0, 0);
+      }
+      // Q^T operands of the dK product, landing under the dV MFMAs
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < KBLK; ++db) a_k[hh][db] = read_tr<DQK>(q_tr, rq, db, qb * 32 + 16 * hh);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
 #pragma unroll
         for (int db = 0; db < KBLK; ++db)
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<DQK>(q_tr, rq, db, qb * 32 + 16 * hh), dsop,
-                                                              dkacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[hh][db], dsop, dkacc[db], 0, 0, 0);
       }
     }
     __syncthreads();
