@@ -364,18 +364,15 @@ template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, KBLK = DQK / 32, VBLK = DV / 32, QB = kTile / 32;
+  // a tile buffer: Q in row and transposed layouts, dO likewise, then LSE
+  // (log2 units) and D for its 64 queries; two buffers alternate
   constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
-  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;   // + lse, D (fp32)
+  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;
   constexpr int STAGE_ELEMS = kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
-  constexpr int LDS_ELEMS = TILE_ELEMS > STAGE_ELEMS ? TILE_ELEMS : STAGE_ELEMS;
+  constexpr int LDS_ELEMS = 2 * TILE_ELEMS > STAGE_ELEMS ? 2 * TILE_ELEMS : STAGE_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
   lds_u16_t* const lds = (lds_u16_t*)smem;
-  lds_u16_t* const q_row = lds;
-  lds_u16_t* const q_tr = lds + Q_ELEMS;
-  lds_u16_t* const do_row = lds + 2 * Q_ELEMS;
-  lds_u16_t* const do_tr = lds + 2 * Q_ELEMS + O_ELEMS;
-  lds_f32_t* const lse_s = (lds_f32_t*)(lds + 2 * Q_ELEMS + 2 * O_ELEMS);
-  lds_f32_t* const d_s = lse_s + kTile;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -415,86 +412,127 @@ void bwd_dkdv_kernel(BwdParams p) {
   TileRegs<DQK> qr;
   TileRegs<DV> dr;
   float rowval = 0.0f;                      // threads 0..63: LSE (log2 units); 64..127: D
-  auto load_tile = [&] __device__ (int q0t) __attribute__((always_inline)) {
+  auto load_tile = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int q0t = qstart + t * kTile;
     tile_load<DQK>(qr, qbase, qk_stride, q0t, L, tid);
     tile_load<DV>(dr, dobase, v_stride, q0t, L, tid);
     const int r = q0t + (tid % kTile);
     if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] * kLog2e : d_h[r]) : 0.0f;
   };
-  load_tile(qstart);
-  for (int t = 0; t < ntiles; ++t) {
-    tile_store<DQK, true, true>(qr, q_row, q_tr, tid);
-    tile_store<DV, true, true>(dr, do_row, do_tr, tid);
-    if (tid < 2 * kTile) lse_s[tid] = rowval;      // lse_s and d_s are adjacent
-    __syncthreads();
+  auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
+  auto stage_tile = [&] __device__ (int t) __attribute__((always_inline)) {
+    lds_u16_t* const base = buf(t);
+    tile_store<DQK, true, true>(qr, base, base + Q_ELEMS, tid);
+    tile_store<DV, true, true>(dr, base + 2 * Q_ELEMS, base + 2 * Q_ELEMS + O_ELEMS, tid);
+    if (tid < 2 * kTile) ((lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS))[tid] = rowval;
+  };
+  // Row operands of the score and dP products of 32-query block nb (block nb
+  // is rows (nb % QB)*32.. of tile nb / QB)
+  bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
+  auto read_sp = [&] __device__ (int nb) __attribute__((always_inline)) {
+    const lds_u16_t* const base = buf(nb / QB);
+    const int qb = nb % QB;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(base, rq, ks, qb);
+#pragma unroll
+    for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + 2 * Q_ELEMS, ro, vs, qb);
+  };
+  auto products_sp = [&] __device__ (f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
+    s = zero;
+    dp = zero;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], kreg[ks], s, 0, 0, 0);
+#pragma unroll
+    for (int vs = 0; vs < V_STEPS; ++vs) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], vreg[vs], dp, 0, 0, 0);
+  };
+
+  // Software pipeline over the 32-query blocks of all tiles: while block nb's
+  // P and dS are computed (VALU), the score and dP products of block nb+1 run
+  // on the matrix cores.  Tiles are double-buffered; before a buffer is
+  // refilled one barrier makes sure no wave still reads the tile it held (two
+  // tiles back), a second makes the new tile visible.
+  const int nblk = ntiles * QB;
+  load_tile(0);
+  stage_tile(0);
+  __syncthreads();
+  if (ntiles > 1) load_tile(1);
+  f32x16_t s_cur, dp_cur;
+  read_sp(0);
+  __builtin_amdgcn_sched_barrier(0);
+  products_sp(s_cur, dp_cur);
+  for (int nb = 0; nb < nblk; ++nb) {
+    const int t = nb / QB, qb = nb % QB;
+    const bool has_next = nb + 1 < nblk;
+    if (has_next && qb == QB - 1) {
+      __syncthreads();
+      stage_tile(t + 1);
+      __syncthreads();
+      if (t + 2 < ntiles) load_tile(t + 2);
+    }
+    const lds_u16_t* const base = buf(t);
+    const lds_f32_t* const lse_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS);
+    const lds_f32_t* const d_s = lse_s + kTile;
     const int q0t = qstart + t * kTile;
-    if (t + 1 < ntiles) load_tile(q0t + kTile);
     const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
+    // dO^T operands of this block's dV product, and the next block's row operands
+    bf16x8_t a_v[2][VBLK], a_k[2][KBLK];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // all LDS operands of the score and dP products first (see the dQ kernel)
-      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS], a_v[2][VBLK], a_k[2][KBLK];
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(q_row, rq, ks, qb);
+      for (int db = 0; db < VBLK; ++db) a_v[hh][db] = read_tr<DV>(base + 2 * Q_ELEMS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+    if (has_next) read_sp(nb + 1);
+    // exponent arguments of this lane's key and queries q0t + qb*32 + 16(r/8) + 8g + r%8
+    float x[16], dd[16];
 #pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(do_row, ro, vs, qb);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16_t s = zero, dp = zero;
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], kreg[ks], s, 0, 0, 0);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], vreg[vs], dp, 0, 0, 0);
-      // dO^T operands of the dV product, landing while P and dS are computed
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < VBLK; ++db) a_v[hh][db] = read_tr<DV>(do_tr, ro, db, qb * 32 + 16 * hh);
-      __builtin_amdgcn_sched_barrier(0);
-      // P and dS for this lane's key and queries q0t + qb*32 + 16(r/8) + 8g + r%8
-      float pv[16], ds[16];
+    for (int r = 0; r < 16; ++r) {
+      const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+      x[r] = __builtin_fmaf(s_cur[r], p.c, -lse_s[qi]);
+      dd[r] = dp_cur[r] - d_s[qi];
+    }
+    if (masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse_s[qi]));
-        if (masked) {
-          const int query = q0t + qi;
-          pv[r] = (key_valid && query < L && (!CAUSAL || key <= query)) ? e : 0.0f;
-        } else {
-          pv[r] = e;
-        }
-        ds[r] = pv[r] * (dp[r] - d_s[qi]);
-      }
-      uint32_t pb[2][4], dsb[2][4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          pb[hh][jj] = pack_bf16x2(pv[8 * hh + 2 * jj], pv[8 * hh + 2 * jj + 1]);
-          dsb[hh][jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
-        }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pb[hh]);
-#pragma unroll
-        for (int db = 0; db < VBLK; ++db)
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[hh][db], pop, dvacc[db], 0, 0, 0);
-      }
-      // Q^T operands of the dK product, landing under the dV MFMAs
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < KBLK; ++db) a_k[hh][db] = read_tr<DQK>(q_tr, rq, db, qb * 32 + 16 * hh);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
-#pragma unroll
-        for (int db = 0; db < KBLK; ++db)
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[hh][db], dsop, dkacc[db], 0, 0, 0);
+        const int query = q0t + qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+        if (!(key_valid && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // one scheduling region: the next block's products, this block's P and
+    // dS, and this block's dV and dK products
+    f32x16_t s_nxt, dp_nxt;
+    products_sp(s_nxt, dp_nxt);        // with no next block: a dropped product of stale operands
+    uint32_t pb[2][4], dsb[2][4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 8 * hh + 2 * jj;
+        const float p0 = __builtin_amdgcn_exp2f(x[r]), p1 = __builtin_amdgcn_exp2f(x[r + 1]);
+        pb[hh][jj] = pack_bf16x2(p0, p1);
+        dsb[hh][jj] = pack_bf16x2(p0 * dd[r], p1 * dd[r + 1]);
+      }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pb[hh]);
+#pragma unroll
+      for (int db = 0; db < VBLK; ++db)
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[hh][db], pop, dvacc[db], 0, 0, 0);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < KBLK; ++db) a_k[hh][db] = read_tr<DQK>(base + Q_ELEMS, rq, db, qb * 32 + 16 * hh);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
+#pragma unroll
+      for (int db = 0; db < KBLK; ++db)
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[hh][db], dsop, dkacc[db], 0, 0, 0);
+    }
+    s_cur = s_nxt;
+    dp_cur = dp_nxt;
   }
+  __syncthreads();                           // the staging area overlaps the tile buffers
   lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
   store_rows<DQK>(dkacc, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
   store_rows<DV>(dvacc, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
