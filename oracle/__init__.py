@@ -19,6 +19,7 @@ Contents
                     and its relative-minimax (Remez) coefficient fit.
 ``attention_backward``  the plain fp64 gradient of softmax attention (dQ, dK,
                     dV and the row term D) by the chain rule.
+``block_sparse``    plain fp64 attention restricted by a 128 x 128 block mask.
 
 Sources (web pages about FlashAttention-4):
   [ainexis]  ainexis.cn deep dive on Tri Dao's FlashAttention-4
@@ -28,18 +29,21 @@ Sources (web pages about FlashAttention-4):
   [jsqmd]    jsqmd.com news "GPU 算力翻倍，AI 反而变慢了？FlashAttention-4 给出了惊人的答案"
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_backward.py`` and ``tests/test_exp2_poly.py`` against closed forms, invariants, an
+``tests/test_oracle_backward.py``, ``tests/test_oracle_block_sparse.py`` and
+``tests/test_exp2_poly.py`` against closed forms, invariants, an
 mpmath brute force and the pages' stated constants; none is
 "parity unpinned".
 """
 from .attention import attention, attention_f64, attention_probs_f64, bf16_bits_to_f64
 from .online_softmax import online_softmax_attention_f64
 from .attention_backward import attention_backward, attention_backward_f64
+from .block_sparse import block_sparse_attention, block_sparse_attention_f64
 from .exp2_poly import (exp2_poly_f64, exp2_poly_f32, remez_exp2_relative,
                         poly_relative_error)
 
 __all__ = [
     "attention", "attention_f64", "attention_probs_f64", "bf16_bits_to_f64",
     "online_softmax_attention_f64", "attention_backward", "attention_backward_f64",
+    "block_sparse_attention", "block_sparse_attention_f64",
     "exp2_poly_f64", "exp2_poly_f32", "remez_exp2_relative", "poly_relative_error",
 ]
