@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
                     [--tau 8.0] [--poly 0] [--no-cpu-baseline] [--bwd]
+                    [--block-density D]
 
 A step is one call of attn_fwd over the whole workload (all query blocks of
 all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
@@ -29,6 +30,12 @@ dQ kernel) instead, on the forward's o and lse and a seeded dO; its
 algorithmic FLOP are 2.5x the forward's (five products of the forward's
 size: S, dP, dV, dK, dQ; the kernels recompute S and dP once more, seven
 products in all).
+
+--block-density D runs the block-sparse forward pass with a seeded random
+128 x 128 block mask keeping each block with probability D; its algorithmic
+FLOP count only the kept blocks, clipped to the sequences (under the causal
+mask a diagonal block counts half and a block above the diagonal nothing, so
+an all-ones mask counts exactly the dense figure).
 """
 from __future__ import annotations
 
@@ -61,6 +68,23 @@ def algorithmic_flops(lengths, H, d_qk, d_v, causal) -> float:
     return tot
 
 
+def block_sparse_flops(lengths, H, d_qk, d_v, causal, mask) -> float:
+    """Algorithmic FLOP of the kept 128 x 128 blocks (mask [B, H, nb, nb])."""
+    import numpy as np
+    tot = 0.0
+    for b, L in enumerate(lengths):
+        nb = (L + 127) // 128
+        if nb == 0:
+            continue
+        size = np.minimum(128, L - 128 * np.arange(nb)).astype(np.float64)      # rows (keys) per block
+        pair = np.outer(size, size)
+        if causal:
+            pair = np.tril(pair, -1) + np.diag(np.diag(pair)) / 2.0
+        kept = mask[b, :, :nb, :nb].astype(np.float64)                           # [H, nb, nb]
+        tot += 2.0 * (d_qk + d_v) * float((kept * pair[None]).sum())
+    return tot
+
+
 def compulsory_bytes(T, H, d_qk, d_v) -> float:
     """Read Q, K, V once, write O (bf16) and LSE (fp32) once."""
     return T * H * (2 * d_qk * 2 + d_v * 2 + d_v * 2 + 4)
@@ -88,7 +112,7 @@ def load_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None) -> dict:
+def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None, block_mask=None) -> dict:
     """Time the fp64 oracle on whole (sequence, head) pairs until the budget is
     spent (the gradient oracle when ``backward_dout`` is given)."""
     import numpy as np
@@ -113,7 +137,13 @@ def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None) -> dict:
         b, h = pairs[idx]
         s, e = int(cu[b]), int(cu[b + 1])
         sub_cu = np.array([0, e - s])
-        if backward_dout is None:
+        if block_mask is not None:
+            oracle.block_sparse_attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
+                                          sub_cu, inp["causal"], inp["scale"],
+                                          np.ascontiguousarray(block_mask[b:b + 1, h:h + 1]))
+            done_flops += block_sparse_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"],
+                                             block_mask[b:b + 1, h:h + 1])
+        elif backward_dout is None:
             oracle.attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
                              sub_cu, inp["causal"], inp["scale"])
             done_flops += algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
@@ -157,6 +187,11 @@ def main():
                          "skip rate and tile counts")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--bwd", action="store_true", help="time the backward pass (attn_bwd) instead")
+    ap.add_argument("--block-density", type=float, default=None,
+                    help="block-sparse forward with a seeded random 128x128 block mask of this density")
+    ap.add_argument("--block-aligned", action="store_true",
+                    help="with --block-density: query-block rows 2i+1 copy rows 2i (the 256-row work items "
+                         "then keep exactly the drawn fraction of key tiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
@@ -202,10 +237,20 @@ def main():
     lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    bmask = bmask_dev = None
+    if args.block_density is not None:
+        if args.bwd:
+            raise SystemExit("--block-density applies to the forward pass")
+        bmask = workloads.make_block_mask(inp["B"], H, inp["N"], args.block_density, seed=0)
+        if args.block_aligned:
+            bmask[:, :, 1::2, :] = bmask[:, :, 0:bmask.shape[2] // 2 * 2:2, :]
+        bmask_dev = torch.from_numpy(bmask).cuda()
+        flops = block_sparse_flops(lengths, H, wl.d_qk, wl.d_v, wl.causal, bmask)
+
     def step():
         ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
                scale=inp["scale"], rescale_threshold_log2=args.tau,
-               poly_exp_sixteenths=args.poly, schedule=args.schedule, stream=stream)
+               poly_exp_sixteenths=args.poly, schedule=args.schedule, block_mask=bmask_dev, stream=stream)
 
     if args.bwd:
         step()                                   # o and lse for the backward pass
@@ -240,9 +285,12 @@ def main():
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
     variant = "bwd" if args.bwd else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
+    if bmask is not None:
+        variant += f",block_density={args.block_density}" + (",aligned" if args.block_aligned else "")
     traffic = None if args.bwd else load_traffic(wl.key, variant)
     out = {
-        "metric": ("attention bwd" if args.bwd else "attention fwd") + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
+        "metric": ("attention bwd" if args.bwd else "attention fwd" if bmask is None else "block-sparse attention fwd")
+                  + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -263,6 +311,8 @@ def main():
                      "traffic": traffic, "kernel_ms": round(ev_ms, 4),
                      "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
     }
+    if bmask is not None:
+        out["config"]["kept_blocks"] = round(float(bmask.mean()), 4)
     if args.bwd:
         out["roofline"]["note"] = "kernel_ms spans the D pass, the dK/dV kernel and the dQ kernel"
         # read q, k, v, o, dO, lse; write dq, dk, dv; D written and read back
@@ -279,7 +329,7 @@ def main():
                         "wave_tiles": tiles, "work_items": items}
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None, bmask)
     print(json.dumps(out), flush=True)
 
 

@@ -51,6 +51,7 @@ class FwdOpts(ctypes.Structure):
         ("poly_exp_sixteenths", ctypes.c_int),
         ("schedule", ctypes.c_int),
         ("stats", ctypes.c_void_p),
+        ("block_mask", ctypes.c_void_p),
     ]
 
 
@@ -143,7 +144,7 @@ def _stream_handle(stream):
 
 def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
         scale=None, rescale_threshold_log2=8.0, poly_exp_sixteenths=0,
-        schedule=SCHEDULE_LONGEST_FIRST, stats=None, stream=None):
+        schedule=SCHEDULE_LONGEST_FIRST, stats=None, block_mask=None, stream=None):
     """Fused attention forward on torch tensors.
 
     Fixed length: q, k [B, N, H, d_qk], v [B, N, H, d_v] (or [T, H, d] with
@@ -153,7 +154,9 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
 
     Returns (o, lse): o bf16 shaped like v, lse fp32 [H, T].  Outputs are
     allocated with torch when not given.  ``stats``: optional uint64/int64
-    device tensor of 4 counters that the kernel adds to.
+    device tensor of 4 counters that the kernel adds to.  ``block_mask``:
+    optional uint8/bool device tensor [B, H, nb, nb], nb = ceil(N / 128), for
+    block-sparse attention (see attn_fwd_opts in include/attn.h).
     """
     import torch
     if q.dim() == 4:
@@ -192,8 +195,14 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d_qk)
+    if block_mask is not None:
+        nb = (N + 127) // 128
+        if (block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous()
+                or not block_mask.is_cuda or tuple(block_mask.shape) != (B, H, nb, nb)):
+            raise ValueError(f"block_mask must be a contiguous uint8/bool CUDA tensor of shape {(B, H, nb, nb)}")
     opts = FwdOpts(float(rescale_threshold_log2), int(poly_exp_sixteenths), int(schedule),
-                   stats.data_ptr() if stats is not None else None)
+                   stats.data_ptr() if stats is not None else None,
+                   block_mask.data_ptr() if block_mask is not None else None)
     st = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  cu_seqlens.data_ptr() if cu_seqlens is not None else None,
                  B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), opts)

@@ -30,6 +30,7 @@ void attn_fwd_opts_default(attn_fwd_opts* opts) {
   opts->poly_exp_sixteenths = 0;
   opts->schedule = ATTN_SCHEDULE_LONGEST_FIRST;
   opts->stats = nullptr;
+  opts->block_mask = nullptr;
 }
 
 const char* attn_strerror(int status) {
@@ -69,6 +70,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   const int np = op.poly_exp_sixteenths;
   if (np != 0 && np != 2 && np != 4 && np != 8) return ATTN_ERR_VALUE;
   if (op.schedule != ATTN_SCHEDULE_LONGEST_FIRST && op.schedule != ATTN_SCHEDULE_NATURAL) return ATTN_ERR_VALUE;
+  if (op.block_mask) {
+    if (d_qk > 128 || np != 0) return ATTN_ERR_UNSUPPORTED;     // 128-key tiles, hardware exp2
+    if (N > 32768) return ATTN_ERR_SHAPE;                       // 256 key blocks of 128
+  }
   if (N == 0) return ATTN_OK;  // no tokens: nothing to do
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_ALIGN;
@@ -101,6 +106,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.tau = op.rescale_threshold_log2;
   p.schedule = op.schedule;
   p.stats = reinterpret_cast<unsigned long long*>(op.stats);
+  p.block_mask = op.block_mask;
+  p.mask_blocks = (int)((N + 127) / 128);
 
   p.next_stride = 0;
   if (op.schedule == ATTN_SCHEDULE_LONGEST_FIRST) {

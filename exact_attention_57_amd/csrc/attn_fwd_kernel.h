@@ -24,6 +24,9 @@ struct FwdParams {
   int next_stride;            // 1-D grid distance to the workgroup that starts next on the
                               // same XCD (the CU count), whose inputs are prefetched; 0: none
   unsigned long long* stats;  // optional device counters [4]
+  const uint8_t* block_mask;  // optional device uint8 [B, H, mask_blocks, mask_blocks]: 128 x 128
+                              // (query block, key block) pairs kept (nonzero) or skipped
+  int mask_blocks;            // ceil(N / 128)
 };
 
 int query_block_rows();

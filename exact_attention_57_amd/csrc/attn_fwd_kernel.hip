@@ -298,10 +298,20 @@ struct False { static constexpr bool value = false; };
 struct Grp0 { static constexpr int value = 0; };
 struct Grp1 { static constexpr int value = 1; };
 
-template <int DQK, int DV, bool CAUSAL, int NPOLY>
+// Block-sparse attention (SPARSE): a byte mask over 128 x 128 (query block,
+// key block) pairs says which score blocks exist.  A workgroup's 256 query
+// rows are two query blocks; it visits the union of their kept key tiles
+// (128 keys each), in order, and a wave skips the tiles its own query block
+// does not keep.  Up to 256 key blocks (N <= 32768) in four 64-bit words.
+constexpr int kMaskBlock = 128;
+constexpr int kMaskWords = 4;
+constexpr int kNoTile = 1 << 20;
+
+template <int DQK, int DV, bool CAUSAL, int NPOLY, bool SPARSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
+  static_assert(!SPARSE || (block_n(DQK) == kMaskBlock && NPOLY == 0), "block-sparse: 128-key tiles, hardware exp");
   constexpr int BN = block_n(DQK);               // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
   using Lay = TileLayout<DQK, DV, BN>;
@@ -374,6 +384,57 @@ void attn_fwd_kernel(FwdParams p) {
   const int t_last = CAUSAL ? min(ntiles - 1, (qw0 + kRowsPerWave - 1) / BN) : ntiles - 1;
   const int qrow = qw0 + lq;
   const bool row_valid = qrow < L;
+
+  // ---- block-sparse: bitmaps (scalar registers, by ballot) of the kept key
+  // tiles among the first ntiles, for the union of the workgroup's two query
+  // blocks (um) and for this wave's own block (own).  nact tiles are visited.
+  uint64_t um[kMaskWords] = {};
+  uint64_t own0 = 0, own1 = 0, own2 = 0, own3 = 0;   // named words: no indexed array in memory
+  int nact = ntiles;
+  if constexpr (SPARSE) {
+    const int nb = p.mask_blocks;
+    const uint8_t* const mrows = p.block_mask + (int64_t)(b * H + h) * nb * nb;
+    const int r0 = 2 * qblk, r1 = 2 * qblk + 1;
+    nact = 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) {
+      const int kb = 64 * w + lane;
+      const bool in = kb < ntiles;
+      const bool a = in && r0 < nb && mrows[(int64_t)r0 * nb + kb] != 0;
+      const bool c = in && r1 < nb && mrows[(int64_t)r1 * nb + kb] != 0;
+      const uint64_t ba = __builtin_amdgcn_ballot_w64(a), bc = __builtin_amdgcn_ballot_w64(c);
+      um[w] = ba | bc;
+      const uint64_t mine = (wave < kWaves / 2) ? ba : bc;
+      if (w == 0) own0 = mine;
+      if (w == 1) own1 = mine;
+      if (w == 2) own2 = mine;
+      if (w == 3) own3 = mine;
+      nact += __builtin_popcountll(um[w]);
+    }
+  }
+  // smallest kept tile above t (kNoTile if none; the identity order when dense)
+  auto next_tile = [&] __device__ (int t) __attribute__((always_inline)) -> int {
+    if constexpr (!SPARSE) {
+      return t + 1;
+    } else {
+      const int first = t + 1;
+      int res = kNoTile;
+#pragma unroll
+      for (int w = kMaskWords - 1; w >= 0; --w) {
+        const int lo = first - 64 * w;
+        uint64_t bits = um[w];
+        if (lo >= 64) bits = 0;
+        else if (lo > 0) bits &= ~0ull << lo;
+        if (bits != 0) res = 64 * w + __builtin_ctzll(bits);
+      }
+      return res;
+    }
+  };
+  static_assert(kMaskWords == 4, "own0..own3");
+  auto own_keeps = [&] __device__ (int t) __attribute__((always_inline)) -> bool {
+    const uint64_t bits = t < 64 ? own0 : t < 128 ? own1 : t < 192 ? own2 : own3;
+    return ((bits >> (t & 63)) & 1ull) != 0;
+  };
 
   // ---- Q^T operand, resident for the whole key loop.  Lane (g, lq) holds
   // Q[qrow][16*ks + 8*g + i], i = 0..7, for every k-step ks.
@@ -629,6 +690,17 @@ void attn_fwd_kernel(FwdParams p) {
   // Softmax of tile t (in sacc): masks, row max, conditional rescale of O and
   // l, P = exp2(c s - m) as bf16 B operands, and the row sums.
   auto softmax = [&] __device__ (int t) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (!own_keeps(t)) {                        // this wave's query block skips tile t
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) pb[kb][hh][jj] = 0u;
+        return;
+      }
+    }
     const int k0 = t * BN;
     // Row max of the tile (raw logits; c > 0 so max commutes with scaling),
     // computed by the matrix phase; a masked tile masks S and takes it again.
@@ -655,7 +727,7 @@ void attn_fwd_kernel(FwdParams p) {
     // every lane rescales its still-zero O and l (alpha = 0).
     const bool need = m_tile > m_run + tau_dec;
     // rescale statistics as wave totals (scalar registers)
-    const bool counted = row_valid && g == 0 && t >= 1 && t <= t_last;
+    const bool counted = !SPARSE && row_valid && g == 0 && t >= 1 && t <= t_last;
     n_considered += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(counted));
     n_taken += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(counted && (need || tau < 0.0f)));
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -674,7 +746,9 @@ void attn_fwd_kernel(FwdParams p) {
     }
     // P = exp2(c s - m) in fp32 (all FMAs before the exponentials, so no exp
     // waits on the FMA just before it), then bf16 B operands and the row sum.
-    const float neg_m = -m_run;
+    // Block-sparse rows can reach a tile with no visible key before any
+    // other (m = -inf, every s = -inf): x must then be -inf, not NaN.
+    const float neg_m = (SPARSE && m_run == -__builtin_inff()) ? 0.0f : -m_run;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -706,28 +780,28 @@ void attn_fwd_kernel(FwdParams p) {
   // free buffer with zeros.  Causal tiles past a wave's diagonal go through the
   // softmax fully masked (P = 0, no rescale), which leaves O, l and m exactly
   // as skipping them would.
-  auto softmax_phase = [&] __device__ (int j) __attribute__((always_inline)) {
-    if (j >= 0 && j < ntiles) softmax(j);
-  };
   auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
     int b0 = 0;                                  // j mod 3
+    // tiles number j-1, j, j+1, j+2 of the visiting order (tile j itself when dense)
+    int t_prev = -1, t_cur = next_tile(-1);
+    int t_n1 = next_tile(t_cur), t_n2 = next_tile(t_n1);
     if (G == 0) prefetch(vbuf(1), kbuf(0));      // operands of matrix(0)
-    for (int j = 0; j <= ntiles; ++j) {
+    for (int j = 0; j <= nact; ++j) {
       const int bm1 = (b0 == 0) ? 2 : b0 - 1;    // (j - 1) mod 3 = (j + 2) mod 3
       const int bp1 = (b0 == 2) ? 0 : b0 + 1;    // (j + 1) mod 3
       const int vc = j & 1, vp = vc ^ 1;         // V buffers of V[j] and V[j-1]
       if (G == 0) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
-        matrix(True{}, vbuf(vp), kbuf(b0), k_tile(j + 2), v_tile(j), kbuf(bm1), vbuf(vc));
+        matrix(True{}, vbuf(vp), kbuf(b0), k_tile(t_n2), v_tile(t_cur), kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         dma_wait_barrier<Lay::ISSUES>();         // K[j+1] has landed
-        softmax_phase(j);
+        if (j < nact) softmax(t_cur);
         prefetch(vbuf(vc), kbuf(bp1));           // operands of matrix(j+1)
         dma_wait_barrier<Lay::K_ISSUES>();       // V[j] has landed
       } else {
-        if (prefetch_next && j == ntiles - 1) prefetch_l2(kbuf(bm1));
-        softmax_phase(j - 1);
+        if (prefetch_next && j == nact - 1) prefetch_l2(kbuf(bm1));
+        if (j >= 1 && j - 1 < nact) softmax(t_prev);
         prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
         barrier();
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
@@ -735,18 +809,23 @@ void attn_fwd_kernel(FwdParams p) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         barrier();
       }
-      n_tiles += (j < ntiles && j <= t_last) ? 1u : 0u;
+      n_tiles += (j < nact && (SPARSE || j <= t_last)) ? 1u : 0u;
       b0 = bp1;
+      t_prev = t_cur;
+      t_cur = t_n1;
+      t_n1 = t_n2;
+      t_n2 = next_tile(t_n2);
     }
   };
   // Prologue: V buffer 1 is read (times P = 0) by matrix(0); the loaders fetch
   // K[0] and K[1] and wait for them before the first barrier.
   for (int i = tid; i < Lay::V_ELEMS / 8; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
   if (grp == 0) {
+    const int t0 = next_tile(-1), t1 = next_tile(t0);
 #pragma unroll
-    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(0), 0u, kbuf(0), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(t0), 0u, kbuf(0), vbuf(0));
 #pragma unroll
-    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(1), 0u, kbuf(1), vbuf(0));
+    for (int d = Lay::V_ISSUES; d < Lay::ISSUES; ++d) dma(d, k_tile(t1), 0u, kbuf(1), vbuf(0));
   }
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -763,7 +842,8 @@ void attn_fwd_kernel(FwdParams p) {
   // every loader's last DMAs have landed.
   barrier();
   const float l_tot = sum_with_partner(l_part);
-  const float inv = 1.0f / l_tot;
+  // a block-sparse row that saw no key: O = 0 (and LSE = -inf + log 0 = -inf)
+  const float inv = (SPARSE && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
   constexpr int OS = DV + 8;                       // staged row stride (elements)
   lds_u16_t* const ost = lds + wave * kRowsPerWave * OS;
 #pragma unroll
@@ -821,6 +901,17 @@ static hipError_t launch_poly(const FwdParams& p, int npoly, hipStream_t s) {
 
 template <int DQK, int DV>
 static hipError_t launch_dims(const FwdParams& p, bool causal, int npoly, hipStream_t s) {
+  if constexpr (block_n(DQK) == kMaskBlock) {
+    if (p.block_mask) {
+      if (npoly != 0) return hipErrorInvalidValue;
+      const dim3 grid = (p.schedule == 0) ? dim3(p.H * p.B * p.n_qblocks) : dim3(p.H, p.B, p.n_qblocks);
+      if (causal) hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, true, 0, true>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, false, 0, true>), grid, dim3(kThreads), 0, s, p);
+      return hipGetLastError();
+    }
+  } else {
+    if (p.block_mask) return hipErrorInvalidValue;
+  }
   return causal ? launch_poly<DQK, DV, true>(p, npoly, s) : launch_poly<DQK, DV, false>(p, npoly, s);
 }
 

@@ -101,8 +101,21 @@ typedef struct attn_fwd_opts {
   /* Optional DEVICE uint64[4] the kernel ADDS to (caller zeroes it):
    * [0] row-tile pairs where a rescale was considered (after a row's first
    * tile), [1] rescales applied, [2] (wave, tile) pairs computed, [3] work
-   * items (query blocks) that ran.  NULL (default) disables counting. */
+   * items (query blocks) that ran.  NULL (default) disables counting.
+   * Counts [0], [1] stay 0 for block-sparse runs. */
   uint64_t* stats;
+  /* Optional DEVICE uint8 block mask for block-sparse attention
+   * (FlexAttention-style variants on the same kernels: wittx news
+   * "FlashAttention-4", section on writing GPU kernels in Python; newton.com.tw
+   * wiki, development history): element [b][h][qb][kb], shape
+   * [B, H, nb, nb] with nb = ceil(N / 128), nonzero keeps the 128 x 128 block
+   * of query rows qb*128.. and keys kb*128.. of sequence b, head h.  Query i
+   * then attends to the keys j of kept blocks (and j <= i if causal); a query
+   * with no such key gets o = 0 and lse = -inf.  Blocks past a sequence's
+   * end are ignored.  Workgroups visit only the key tiles some of their rows
+   * keep.  Requires d_qk <= 128, N <= 32768 and poly_exp_sixteenths = 0
+   * (else ATTN_ERR_UNSUPPORTED / ATTN_ERR_SHAPE).  NULL (default): dense. */
+  const uint8_t* block_mask;
 } attn_fwd_opts;
 
 /* Fill *opts with the defaults above. */

@@ -154,3 +154,18 @@ def call_bwd(**kw):
 def test_bwd_validation_codes(kw, code):
     assert call_bwd(**kw) == code
 
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_qk=192, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(poly=2), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(N=32769), ea.ATTN_ERR_SHAPE),
+    (dict(N=0, q=None, k=None, v=None, o=None, lse=None), ea.ATTN_OK),
+])
+def test_block_mask_validation(kw, code):
+    o = ea.default_opts()
+    assert o.block_mask is None
+    o.block_mask = P
+    if "poly" in kw:
+        o.poly_exp_sixteenths = kw.pop("poly")
+    assert call(opts=o, **kw) == code
+

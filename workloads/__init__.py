@@ -30,6 +30,7 @@ import numpy as np
 
 __all__ = [
     "make_output_grad",
+    "make_block_mask",
     "Workload",
     "WORKLOADS",
     "workload",
@@ -248,4 +249,13 @@ def make_output_grad(inp: dict, seed: int = 0) -> np.ndarray:
     """Seeded N(0, 1) bf16 output gradient dO [T, H, d_v] for an input dict
     (its own random stream, independent of q, k, v)."""
     return _normal_bf16(seed, 3, (int(inp["T"]), int(inp["H"]), int(inp["d_v"])))
+
+
+def make_block_mask(B: int, H: int, N: int, density: float, seed: int = 0) -> np.ndarray:
+    """Seeded random uint8 block mask [B, H, nb, nb], nb = ceil(N / 128): each
+    128 x 128 (query block, key block) pair is kept with probability
+    ``density`` (independent draws from their own random stream)."""
+    nb = (int(N) + 127) // 128
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(4,)))
+    return (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
 
