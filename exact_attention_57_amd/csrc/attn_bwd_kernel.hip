@@ -20,11 +20,13 @@
 // score and dP tiles it needs (7 matrix products instead of 5), and the
 // results are bitwise reproducible run to run.
 //
-// Layout of the work on the chip: a workgroup is 4 wave64s, one per SIMD,
-// each owning 32 rows of its block; a 64-row tile of the streamed operands
-// (Q and dO for dK/dV, K and V for dQ) is staged in LDS once per workgroup
-// and read by all four waves, while the next tile's global loads are in
-// flight.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
+// Layout of the work on the chip: a workgroup is 4 wave64s, each owning 32
+// rows of its block; a 64-row tile of the streamed operands (Q and dO for
+// dK/dV, K and V for dQ) is staged in LDS once per workgroup and read by all
+// four waves.  The dK/dV kernel (over 256 registers per wave: one wave per
+// SIMD) double-buffers its tiles and software-pipelines its blocks; the dQ
+// kernel fits in 256 registers, so two workgroups share a CU and the SIMDs
+// interleave their waves.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
 // accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
@@ -240,7 +242,7 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
 
 // ---- dQ: one workgroup per block of 128 query rows of one (sequence, head).
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
   constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
@@ -288,45 +290,29 @@ void bwd_dq_kernel(BwdParams p) {
 
   TileRegs<DQK> kr;
   TileRegs<DV> vr;
-  tile_load<DQK>(kr, kbase, qk_stride, 0, L, tid);
-  tile_load<DV>(vr, vbase, v_stride, 0, L, tid);
   for (int t = 0; t < ntiles; ++t) {
+    // no register-held prefetch of the next tile: two workgroups share a CU,
+    // and the other one computes while this one loads
+    tile_load<DQK>(kr, kbase, qk_stride, t * kTile, L, tid);
+    tile_load<DV>(vr, vbase, v_stride, t * kTile, L, tid);
     tile_store<DQK, true, true>(kr, k_row, k_tr, tid);
     tile_store<DV, true, false>(vr, v_row, v_row, tid);
     __syncthreads();
-    if (t + 1 < ntiles) {
-      tile_load<DQK>(kr, kbase, qk_stride, (t + 1) * kTile, L, tid);
-      tile_load<DV>(vr, vbase, v_stride, (t + 1) * kTile, L, tid);
-    }
     const int k0 = t * kTile;
-    // masks only where the tile reaches past the sequence end or the
-    // wave's diagonal, or the wave has rows past the end
     const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      // every LDS operand of the score and dP products is requested before
-      // the first of them, so the MFMAs queue behind the reads instead of
-      // each waiting out a read's latency
-      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS], a_q[2][QBLK];
+      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
 #pragma unroll
       for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(k_row, rk, ks, kb);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
-      __builtin_amdgcn_sched_barrier(0);
       f32x16_t s = zero, dp = zero;
 #pragma unroll
       for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], qreg[ks], s, 0, 0, 0);
 #pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
+#pragma unroll
       for (int vs = 0; vs < V_STEPS; ++vs)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
-      // K^T operands of the dQ product: requested now, they land while the
-      // exponentials run
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < QBLK; ++db) a_q[hh][db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
-      __builtin_amdgcn_sched_barrier(0);
-      // dS^T for this lane's query and keys k0 + kb*32 + 16(r/8) + 8g + r%8
       float ds[16];
       if (masked) {
 #pragma unroll
@@ -341,17 +327,18 @@ void bwd_dq_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r)
           ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) * (dp[r] - dq_row);
       }
-      uint32_t dsb[2][4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dsb[hh][jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
+        uint32_t dsb[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dsb[jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
+        bf16x8_t a_q[QBLK];
+#pragma unroll
+        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
 #pragma unroll
         for (int db = 0; db < QBLK; ++db)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[hh][db], bop, dqacc[db], 0, 0, 0);
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
       }
     }
     __syncthreads();
