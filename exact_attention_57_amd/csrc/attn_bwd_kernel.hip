@@ -20,18 +20,18 @@
 // score and dP tiles it needs (7 matrix products instead of 5), and the
 // results are bitwise reproducible run to run.
 //
-// Layout of the work on the chip: a workgroup is 4 wave64s, each owning 32
-// rows of its block; a 64-row tile of the streamed operands (Q and dO for
-// dK/dV, K and V for dQ) is staged in LDS once per workgroup and read by all
-// four waves.  The dK/dV kernel (over 256 registers per wave: one wave per
-// SIMD) double-buffers its tiles and software-pipelines its blocks; the dQ
-// kernel fits in 256 registers, so two workgroups share a CU and the SIMDs
-// interleave their waves.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
+// Layout of the work on the chip: each wave owns 32 rows of its workgroup's
+// block; a 64-row tile of the streamed operands (Q and dO for dK/dV, K and V
+// for dQ) is staged in LDS once per workgroup and read by all its waves.
+// Both kernels keep every wave within 256 registers so that each SIMD runs
+// two waves: the dQ kernel as two 4-wave workgroups per CU, the dK/dV kernel
+// as one 8-wave workgroup whose two halves split the products between them.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
 // accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
 //   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V in registers)
-//               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read)
+//               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read),
+//               S, P, dV^T in one wave group and dP, dS, dK^T in the other
 // With the streamed tile's rows read in an order with bits 2 and 3 of the
 // row index swapped, accumulator registers 0..7 and 8..15 of a 32 x 32
 // block hold 8 consecutive rows -- the B-operand slots of the next product --
@@ -136,28 +136,28 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdParams p) {
 }
 
 // ---- tiles: global -> registers (rows past L read as zeros) -> LDS.
-template <int D>
+template <int D, int NT = kThreads>
 struct TileRegs {
-  static constexpr int N = kTile * D / 8 / kThreads;
+  static constexpr int N = kTile * D / 8 / NT;
   u32x4_t c[N];
 };
-template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D>& t, const uint16_t* base, int64_t row_stride, int row0, int L,
-                                          int tid) {
+template <int D, int NT = kThreads>
+__device__ __forceinline__ void tile_load(TileRegs<D, NT>& t, const uint16_t* base, int64_t row_stride, int row0,
+                                          int L, int tid) {
   constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::N; ++i) {
-    const int idx = i * kThreads + tid, r = idx / CPR, ch = idx % CPR;
+  for (int i = 0; i < TileRegs<D, NT>::N; ++i) {
+    const int idx = i * NT + tid, r = idx / CPR, ch = idx % CPR;
     const int row = row0 + r;
     t.c[i] = (row < L) ? *(const u32x4_t*)(base + (int64_t)row * row_stride + ch * 8) : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
-template <int D, bool ROW, bool TR>
-__device__ __forceinline__ void tile_store(const TileRegs<D>& t, lds_u16_t* row_l, lds_u16_t* tr_l, int tid) {
+template <int D, bool ROW, bool TR, int NT = kThreads>
+__device__ __forceinline__ void tile_store(const TileRegs<D, NT>& t, lds_u16_t* row_l, lds_u16_t* tr_l, int tid) {
   constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::N; ++i) {
-    const int idx = i * kThreads + tid, r = idx / CPR, ch = idx % CPR;
+  for (int i = 0; i < TileRegs<D, NT>::N; ++i) {
+    const int idx = i * NT + tid, r = idx / CPR, ch = idx % CPR;
     if (ROW) *(lds_u32x4_t*)(row_l + r * D + ((ch ^ RowSwz<D>::f(r)) * 8)) = t.c[i];
     if (TR) *(lds_u32x4_t*)(tr_l + r * D + ((ch ^ TrSwz<D>::f(r)) * 8)) = t.c[i];
   }
@@ -346,23 +346,38 @@ void bwd_dq_kernel(BwdParams p) {
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
 
-// ---- dK, dV: one workgroup per block of 128 key rows of one (sequence, head).
+// ---- dK, dV with the work split over two wave groups: one workgroup of 8
+// waves per block of 128 key rows.  Waves 0-3 (dV group) own 32 keys each and
+// compute S = Q K^T, P and dV^T += dO^T P; waves 4-7 (dK group) own the same
+// keys and compute dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS, taking P
+// from the dV wave of their key slice through LDS (as bf16, lane for lane:
+// both accumulators hold one key per lane and the same queries per
+// register).  Each wave fits in 256 registers, so every SIMD holds one wave
+// of each group and the matrix cores interleave them; each group runs 16
+// MFMAs per 32-query block, the same 32 in total as one wave doing all four
+// products.  One barrier per block separates P's writer from its reader:
+//   dV group: ... | dV(b), S(b+1), P(b+1) -> LDS | dV(b+1), S(b+2) ...
+//   dK group: ... | dS(b), dK(b), dP(b+1)       | dS(b+1), dK(b+1) ...
+// P alternates between two LDS buffers, the Q/dO tiles between two more.
+constexpr int kThreads2 = 2 * kThreads;
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_split_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, KBLK = DQK / 32, VBLK = DV / 32, QB = kTile / 32;
-  // a tile buffer: Q in row and transposed layouts, dO likewise, then LSE
-  // (log2 units) and D for its 64 queries; two buffers alternate
   constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
-  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;
-  constexpr int STAGE_ELEMS = kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
-  constexpr int LDS_ELEMS = 2 * TILE_ELEMS > STAGE_ELEMS ? 2 * TILE_ELEMS : STAGE_ELEMS;
+  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;   // + LSE (log2 units), D
+  constexpr int P_ELEMS = kWaves * kWave * 16;                          // 32 x 32 bf16 per dV wave
+  constexpr int STAGE_ELEMS = 2 * kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
+  constexpr int WORK_ELEMS = 2 * TILE_ELEMS + 2 * P_ELEMS;
+  constexpr int LDS_ELEMS = WORK_ELEMS > STAGE_ELEMS ? WORK_ELEMS : STAGE_ELEMS;
   static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
   lds_u16_t* const lds = (lds_u16_t*)smem;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool kgrp = wave >= kWaves;          // dK group
+  const int wv = wave % kWaves;              // key slice of the wave within its group
   const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
   const int blk = blockIdx.x % p.n_blocks, bh = blockIdx.x / p.n_blocks;
   const int h = bh % p.H, b = bh / p.H;
@@ -370,18 +385,20 @@ void bwd_dkdv_kernel(BwdParams p) {
   seq_range(p, b, seq0, L);
   const int k0 = blk * kBlock;
   if (k0 >= L) return;
-  const int kw0 = k0 + wave * kRows;
+  const int kw0 = k0 + wv * kRows;
   const int key = kw0 + lq;
   const bool key_valid = key < L;
 
-  bf16x8_t kreg[QK_STEPS], vreg[V_STEPS];
-  load_b_operand<DQK>(kreg, p.k, seq0 + key, p.H, h, g, key_valid);
-  load_b_operand<DV>(vreg, p.v, seq0 + key, p.H, h, g, key_valid);
+  // dV group: K rows of its keys (B operand of S); dK group: V rows (of dP)
+  bf16x8_t breg[(QK_STEPS > V_STEPS) ? QK_STEPS : V_STEPS];
+  if (kgrp) load_b_operand<DV>(*(bf16x8_t(*)[V_STEPS])breg, p.v, seq0 + key, p.H, h, g, key_valid);
+  else load_b_operand<DQK>(*(bf16x8_t(*)[QK_STEPS])breg, p.k, seq0 + key, p.H, h, g, key_valid);
 
   const Reads<DQK> rq(lane);
   const Reads<DV> ro(lane);
   const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
   const int ntiles = (L - qstart + kTile - 1) / kTile;
+  const int nblk = ntiles * QB;
   const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
   const uint16_t* const qbase = p.q + (int64_t)seq0 * qk_stride + (int64_t)h * DQK;
   const uint16_t* const dobase = p.dout + (int64_t)seq0 * v_stride + (int64_t)h * DV;
@@ -389,140 +406,160 @@ void bwd_dkdv_kernel(BwdParams p) {
   const float* const lse_h = p.lse + (int64_t)h * T + seq0;
   const float* const d_h = p.delta + (int64_t)h * T + seq0;
 
-  f32x16_t dkacc[KBLK], dvacc[VBLK];
+  constexpr int ABLK = KBLK > VBLK ? KBLK : VBLK;
+  f32x16_t acc[ABLK];                        // dK^T blocks (dK group) or dV^T blocks (dV group)
 #pragma unroll
-  for (int i = 0; i < KBLK; ++i) dkacc[i] = f32x16_t{};
-#pragma unroll
-  for (int i = 0; i < VBLK; ++i) dvacc[i] = f32x16_t{};
+  for (int i = 0; i < ABLK; ++i) acc[i] = f32x16_t{};
   const f32x16_t zero = {};
 
-  TileRegs<DQK> qr;
-  TileRegs<DV> dr;
+  TileRegs<DQK, kThreads2> qr;
+  TileRegs<DV, kThreads2> dr;
   float rowval = 0.0f;                      // threads 0..63: LSE (log2 units); 64..127: D
   auto load_tile = [&] __device__ (int t) __attribute__((always_inline)) {
     const int q0t = qstart + t * kTile;
-    tile_load<DQK>(qr, qbase, qk_stride, q0t, L, tid);
-    tile_load<DV>(dr, dobase, v_stride, q0t, L, tid);
+    tile_load<DQK, kThreads2>(qr, qbase, qk_stride, q0t, L, tid);
+    tile_load<DV, kThreads2>(dr, dobase, v_stride, q0t, L, tid);
     const int r = q0t + (tid % kTile);
     if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] * kLog2e : d_h[r]) : 0.0f;
   };
   auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
   auto stage_tile = [&] __device__ (int t) __attribute__((always_inline)) {
     lds_u16_t* const base = buf(t);
-    tile_store<DQK, true, true>(qr, base, base + Q_ELEMS, tid);
-    tile_store<DV, true, true>(dr, base + 2 * Q_ELEMS, base + 2 * Q_ELEMS + O_ELEMS, tid);
+    tile_store<DQK, true, true, kThreads2>(qr, base, base + Q_ELEMS, tid);
+    tile_store<DV, true, true, kThreads2>(dr, base + 2 * Q_ELEMS, base + 2 * Q_ELEMS + O_ELEMS, tid);
     if (tid < 2 * kTile) ((lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS))[tid] = rowval;
   };
-  // Row operands of the score and dP products of 32-query block nb (block nb
-  // is rows (nb % QB)*32.. of tile nb / QB)
-  bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
-  auto read_sp = [&] __device__ (int nb) __attribute__((always_inline)) {
-    const lds_u16_t* const base = buf(nb / QB);
-    const int qb = nb % QB;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(base, rq, ks, qb);
-#pragma unroll
-    for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + 2 * Q_ELEMS, ro, vs, qb);
-  };
-  auto products_sp = [&] __device__ (f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
-    s = zero;
-    dp = zero;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], kreg[ks], s, 0, 0, 0);
-#pragma unroll
-    for (int vs = 0; vs < V_STEPS; ++vs) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], vreg[vs], dp, 0, 0, 0);
+  // this lane's 32 bytes of the P block of key slice wv, buffer i
+  auto pslot = [&] __device__ (int i) __attribute__((always_inline)) {
+    return (lds_u32x4_t*)(lds + 2 * TILE_ELEMS + i * P_ELEMS + (wv * kWave + lane) * 16);
   };
 
-  // Software pipeline over the 32-query blocks of all tiles: while block nb's
-  // P and dS are computed (VALU), the score and dP products of block nb+1 run
-  // on the matrix cores.  Tiles are double-buffered; before a buffer is
-  // refilled one barrier makes sure no wave still reads the tile it held (two
-  // tiles back), a second makes the new tile visible.
-  const int nblk = ntiles * QB;
-  load_tile(0);
-  stage_tile(0);
-  __syncthreads();
-  if (ntiles > 1) load_tile(1);
-  f32x16_t s_cur, dp_cur;
-  read_sp(0);
-  __builtin_amdgcn_sched_barrier(0);
-  products_sp(s_cur, dp_cur);
-  for (int nb = 0; nb < nblk; ++nb) {
+  // carried from a block's first half to its second, in the same registers:
+  // the dK group's dP (16 floats) or the dV group's P (8 dwords of bf16 pairs)
+  f32x16_t carry = zero;
+  // first half of block nb: dV group S, P -> LDS; dK group dP
+  auto half_a = [&] __device__ (int nb) __attribute__((always_inline)) {
     const int t = nb / QB, qb = nb % QB;
-    const bool has_next = nb + 1 < nblk;
-    if (has_next && qb == QB - 1) {
-      __syncthreads();
-      stage_tile(t + 1);
-      __syncthreads();
-      if (t + 2 < ntiles) load_tile(t + 2);
-    }
     const lds_u16_t* const base = buf(t);
-    const lds_f32_t* const lse_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS);
-    const lds_f32_t* const d_s = lse_s + kTile;
-    const int q0t = qstart + t * kTile;
-    const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
-    // dO^T operands of this block's dV product, and the next block's row operands
-    bf16x8_t a_v[2][VBLK], a_k[2][KBLK];
+    if (!kgrp) {
+      bf16x8_t a_s[QK_STEPS];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(base, rq, ks, qb);
+      f32x16_t s = zero;
 #pragma unroll
-      for (int db = 0; db < VBLK; ++db) a_v[hh][db] = read_tr<DV>(base + 2 * Q_ELEMS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
-    if (has_next) read_sp(nb + 1);
-    // exponent arguments of this lane's key and queries q0t + qb*32 + 16(r/8) + 8g + r%8
-    float x[16], dd[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-      x[r] = __builtin_fmaf(s_cur[r], p.c, -lse_s[qi]);
-      dd[r] = dp_cur[r] - d_s[qi];
-    }
-    if (masked) {
+      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], breg[ks], s, 0, 0, 0);
+      const lds_f32_t* const lse_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS);
+      const int q0t = qstart + t * kTile;
+      const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
+      float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int query = q0t + qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-        if (!(key_valid && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
+        const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+        x[r] = __builtin_fmaf(s[r], p.c, -lse_s[qi]);
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int query = q0t + qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+          if (!(key_valid && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
+        }
+      }
+      uint32_t pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * i]), __builtin_amdgcn_exp2f(x[2 * i + 1]));
+        carry[i] = __uint_as_float(pw[i]);
+      }
+      lds_u32x4_t* const slot = pslot(nb & 1);
+      slot[0] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+      slot[1] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
+    } else {
+      bf16x8_t a_p[V_STEPS];
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + 2 * Q_ELEMS, ro, vs, qb);
+      carry = zero;
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs)
+        carry = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], breg[vs], carry, 0, 0, 0);
+    }
+  };
+  // second half of block nb: dV group dV; dK group P from LDS, dS, dK
+  auto half_b = [&] __device__ (int nb) __attribute__((always_inline)) {
+    const int t = nb / QB, qb = nb % QB;
+    const lds_u16_t* const base = buf(t);
+    if (!kgrp) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t pw[4] = {__float_as_uint(carry[4 * hh]), __float_as_uint(carry[4 * hh + 1]),
+                                __float_as_uint(carry[4 * hh + 2]), __float_as_uint(carry[4 * hh + 3])};
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw);
+        bf16x8_t a_v[VBLK];
+#pragma unroll
+        for (int db = 0; db < VBLK; ++db) a_v[db] = read_tr<DV>(base + 2 * Q_ELEMS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+#pragma unroll
+        for (int db = 0; db < VBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[db], bop, acc[db], 0, 0, 0);
+      }
+    } else {
+      const lds_f32_t* const d_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS) + kTile;
+      const lds_u32x4_t* const slot = pslot(nb & 1);
+      const u32x4_t praw[2] = {slot[0], slot[1]};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t dsb[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 8 * hh + 2 * jj;
+          const int qi = qb * 32 + 16 * hh + 8 * g + 2 * jj;
+          const uint32_t w = praw[hh][jj];
+          dsb[jj] = pack_bf16x2(bf16_lo(w) * (carry[r] - d_s[qi]), bf16_hi(w) * (carry[r + 1] - d_s[qi + 1]));
+        }
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
+        bf16x8_t a_k[KBLK];
+#pragma unroll
+        for (int db = 0; db < KBLK; ++db) a_k[db] = read_tr<DQK>(base + Q_ELEMS, rq, db, qb * 32 + 16 * hh);
+#pragma unroll
+        for (int db = 0; db < KBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[db], bop, acc[db], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // one scheduling region: the next block's products, this block's P and
-    // dS, and this block's dV and dK products
-    f32x16_t s_nxt, dp_nxt;
-    products_sp(s_nxt, dp_nxt);        // with no next block: a dropped product of stale operands
-    uint32_t pb[2][4], dsb[2][4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 8 * hh + 2 * jj;
-        const float p0 = __builtin_amdgcn_exp2f(x[r]), p1 = __builtin_amdgcn_exp2f(x[r + 1]);
-        pb[hh][jj] = pack_bf16x2(p0, p1);
-        dsb[hh][jj] = pack_bf16x2(p0 * dd[r], p1 * dd[r + 1]);
+  };
+
+  // Tiles: both buffers filled up front; tile u+1 goes into the buffer of tile
+  // u-1 after barrier 2u (u >= 1), when every wave has finished block 2u-1,
+  // and is visible from barrier 2u+1 on, before block 2u+2 reads it.
+  load_tile(0);
+  stage_tile(0);
+  if (ntiles > 1) {
+    load_tile(1);
+    stage_tile(1);
+  }
+  if (ntiles > 2) load_tile(2);
+  __syncthreads();
+  half_a(0);
+  for (int nb = 0; nb < nblk; ++nb) {
+    __syncthreads();
+    if (nb % QB == 0 && nb >= QB) {
+      const int u = nb / QB;
+      if (u + 1 < ntiles) {
+        stage_tile(u + 1);
+        if (u + 2 < ntiles) load_tile(u + 2);
       }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pb[hh]);
-#pragma unroll
-      for (int db = 0; db < VBLK; ++db)
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[hh][db], pop, dvacc[db], 0, 0, 0);
     }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int db = 0; db < KBLK; ++db) a_k[hh][db] = read_tr<DQK>(base + Q_ELEMS, rq, db, qb * 32 + 16 * hh);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8_t dsop = __builtin_bit_cast(bf16x8_t, dsb[hh]);
-#pragma unroll
-      for (int db = 0; db < KBLK; ++db)
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[hh][db], dsop, dkacc[db], 0, 0, 0);
-    }
-    s_cur = s_nxt;
-    dp_cur = dp_nxt;
+    half_b(nb);
+    if (nb + 1 < nblk) half_a(nb + 1);
   }
   __syncthreads();                           // the staging area overlaps the tile buffers
   lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
-  store_rows<DQK>(dkacc, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
-  store_rows<DV>(dvacc, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+  if (kgrp) {
+    f32x16_t dk[KBLK];
+#pragma unroll
+    for (int i = 0; i < KBLK; ++i) dk[i] = acc[i];
+    store_rows<DQK>(dk, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+  } else {
+    f32x16_t dv[VBLK];
+#pragma unroll
+    for (int i = 0; i < VBLK; ++i) dv[i] = acc[i];
+    store_rows<DV>(dv, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+  }
 }
 
 template <int DQK, int DV>
@@ -532,10 +569,10 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, s, p);
   const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
   if (causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
