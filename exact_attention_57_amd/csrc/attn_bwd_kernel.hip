@@ -108,6 +108,25 @@ __device__ __forceinline__ void seq_range(const BwdParams& p, int b, int& seq0, 
   }
 }
 
+// Work decode of a 1-D grid of W = B*H*n_blocks workgroups.  The hardware
+// deals workgroup i to XCD i mod 8; XCD x takes a contiguous run of a list
+// ordered by (head, sequence) pair and block within the pair, so the blocks
+// of one pair run on one XCD and share its L2 for the pair's streamed tiles.
+// reverse: blocks of a pair in decreasing order (longest first for the
+// causal dQ kernel, whose block b visits b+1 key tiles).
+constexpr int kXcds = 8;
+__device__ __forceinline__ void decode_block(const BwdParams& p, bool reverse, int& h, int& b, int& blk) {
+  const int W = p.B * p.H * p.n_blocks;
+  const int i = blockIdx.x;
+  const int x = i % kXcds, slot = i / kXcds;
+  const int g = x * (W / kXcds) + min(x, W % kXcds) + slot;
+  const int pair = g / p.n_blocks;
+  blk = g - pair * p.n_blocks;
+  if (reverse) blk = p.n_blocks - 1 - blk;
+  h = pair / p.B;
+  b = pair - h * p.B;
+}
+
 // Row sigma(m): m with bits 2 and 3 swapped.
 __device__ __forceinline__ int sigma(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -258,8 +277,8 @@ void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
-  const int blk = blockIdx.x % p.n_blocks, bh = blockIdx.x / p.n_blocks;
-  const int h = bh % p.H, b = bh / p.H;
+  int h, b, blk;
+  decode_block(p, CAUSAL, h, b, blk);
   int seq0, L;
   seq_range(p, b, seq0, L);
   const int q0 = blk * kBlock;
@@ -274,6 +293,8 @@ void bwd_dq_kernel(BwdParams p) {
   const int T = total_tokens(p);
   const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
   const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
+  // last key this lane's query sees (-1: none, the row is past the end)
+  const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
 
   const Reads<DQK> rk(lane);
   const Reads<DV> rv(lane);
@@ -314,18 +335,14 @@ void bwd_dq_kernel(BwdParams p) {
       for (int vs = 0; vs < V_STEPS; ++vs)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
       float ds[16];
-      if (masked) {
+      {
+        // keys visible to this lane's query: up to key_lim (offsets within the block)
+        const int lim = masked ? key_lim - (k0 + kb * 32 + 8 * g) : 64;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-          const bool ok = row_valid && key < L && (!CAUSAL || key <= qrow);
-          const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) : 0.0f;
-          ds[r] = pv * (dp[r] - dq_row);
+          const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
+          ds[r] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2)) * (dp[r] - dq_row);
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -379,8 +396,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   const bool kgrp = wave >= kWaves;          // dK group
   const int wv = wave % kWaves;              // key slice of the wave within its group
   const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
-  const int blk = blockIdx.x % p.n_blocks, bh = blockIdx.x / p.n_blocks;
-  const int h = bh % p.H, b = bh / p.H;
+  int h, b, blk;
+  decode_block(p, false, h, b, blk);
   int seq0, L;
   seq_range(p, b, seq0, L);
   const int k0 = blk * kBlock;
