@@ -20,6 +20,7 @@ Contents
 ``attention_backward``  the plain fp64 gradient of softmax attention (dQ, dK,
                     dV and the row term D) by the chain rule.
 ``block_sparse``    plain fp64 attention restricted by a 128 x 128 block mask.
+``fp8``             the OCP E4M3 decode and attention of dequantised FP8 inputs.
 
 Sources (web pages about FlashAttention-4):
   [ainexis]  ainexis.cn deep dive on Tri Dao's FlashAttention-4
@@ -29,7 +30,7 @@ Sources (web pages about FlashAttention-4):
   [jsqmd]    jsqmd.com news "GPU 算力翻倍，AI 反而变慢了？FlashAttention-4 给出了惊人的答案"
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_backward.py``, ``tests/test_oracle_block_sparse.py`` and
+``tests/test_oracle_backward.py``, ``tests/test_oracle_block_sparse.py``, ``tests/test_oracle_fp8.py`` and
 ``tests/test_exp2_poly.py`` against closed forms, invariants, an
 mpmath brute force and the pages' stated constants; none is
 "parity unpinned".
@@ -38,6 +39,7 @@ from .attention import attention, attention_f64, attention_probs_f64, bf16_bits_
 from .online_softmax import online_softmax_attention_f64
 from .attention_backward import attention_backward, attention_backward_f64
 from .block_sparse import block_sparse_attention, block_sparse_attention_f64
+from .fp8 import attention_fp8, e4m3_to_f64
 from .exp2_poly import (exp2_poly_f64, exp2_poly_f32, remez_exp2_relative,
                         poly_relative_error)
 
@@ -46,4 +48,5 @@ __all__ = [
     "online_softmax_attention_f64", "attention_backward", "attention_backward_f64",
     "block_sparse_attention", "block_sparse_attention_f64",
     "exp2_poly_f64", "exp2_poly_f32", "remez_exp2_relative", "poly_relative_error",
+    "attention_fp8", "e4m3_to_f64",
 ]

@@ -259,3 +259,26 @@ def make_block_mask(B: int, H: int, N: int, density: float, seed: int = 0) -> np
     rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(4,)))
     return (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
 
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the OCP E4M3 8-bit float (nearest even; values
+    beyond 448 saturate to +-448) and return the uint8 bit patterns.  Input
+    preparation only: torch's own float8_e4m3fn conversion on the CPU."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = torch.clamp(t, -448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_fp8_inputs(inp: dict, prescale=(1.0, 1.0, 1.0)) -> dict:
+    """FP8 copies of an input dict's bf16 q, k, v: each tensor is multiplied
+    by its ``prescale`` factor, rounded to E4M3 codes, and paired with the
+    dequantisation factor 1/prescale.  Returns a new dict with q8, k8, v8
+    (uint8) and q_descale, k_descale, v_descale, plus the shape fields."""
+    out = {key: val for key, val in inp.items() if key not in ("q", "k", "v")}
+    for name, f in zip(("q", "k", "v"), prescale):
+        x = bf16_bits_to_f32(inp[name]) * np.float32(f)
+        out[name + "8"] = f32_to_e4m3_codes(x)
+        out[name + "_descale"] = float(np.float32(1.0) / np.float32(f))
+    return out
