@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
                     [--tau 8.0] [--poly 0] [--no-cpu-baseline] [--bwd]
-                    [--block-density D]
+                    [--block-density D] [--fp8]
 
 A step is one call of attn_fwd over the whole workload (all query blocks of
 all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
@@ -36,6 +36,10 @@ products in all).
 FLOP count only the kept blocks, clipped to the sequences (under the causal
 mask a diagonal block counts half and a block above the diagonal nothing, so
 an all-ones mask counts exactly the dense figure).
+
+--fp8 runs the FP8 forward pass (attn_fwd_fp8) on the same draws rounded to
+E4M3 (descales 1); same FLOP convention, roofline against the dense FP8
+MFMA peak (5.0 PFLOP/s), with the percentage of the bf16 peak alongside.
 """
 from __future__ import annotations
 
@@ -50,6 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "noncausal_b4h16n4096d128"
 KERNEL_SOURCES = ["exact_attention_57_amd/csrc/attn_fwd_kernel.hip"]
@@ -112,7 +117,7 @@ def load_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None, block_mask=None) -> dict:
+def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None, block_mask=None, fp8=None) -> dict:
     """Time the fp64 oracle on whole (sequence, head) pairs until the budget is
     spent (the gradient oracle when ``backward_dout`` is given)."""
     import numpy as np
@@ -137,7 +142,11 @@ def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None, block_mask=Non
         b, h = pairs[idx]
         s, e = int(cu[b]), int(cu[b + 1])
         sub_cu = np.array([0, e - s])
-        if block_mask is not None:
+        if fp8 is not None:
+            oracle.attention_fp8(fp8["q8"][s:e, h:h + 1], fp8["k8"][s:e, h:h + 1], fp8["v8"][s:e, h:h + 1],
+                                 sub_cu, inp["causal"], inp["scale"])
+            done_flops += algorithmic_flops([e - s], 1, inp["d_qk"], inp["d_v"], inp["causal"])
+        elif block_mask is not None:
             oracle.block_sparse_attention(inp["q"][s:e, h:h + 1], inp["k"][s:e, h:h + 1], inp["v"][s:e, h:h + 1],
                                           sub_cu, inp["causal"], inp["scale"],
                                           np.ascontiguousarray(block_mask[b:b + 1, h:h + 1]))
@@ -192,6 +201,7 @@ def main():
     ap.add_argument("--block-aligned", action="store_true",
                     help="with --block-density: query-block rows 2i+1 copy rows 2i (the 256-row work items "
                          "then keep exactly the drawn fraction of key tiles)")
+    ap.add_argument("--fp8", action="store_true", help="time the FP8 (E4M3) forward pass (attn_fwd_fp8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
@@ -252,6 +262,17 @@ def main():
                scale=inp["scale"], rescale_threshold_log2=args.tau,
                poly_exp_sixteenths=args.poly, schedule=args.schedule, block_mask=bmask_dev, stream=stream)
 
+    f8 = None
+    if args.fp8:
+        if args.bwd or args.block_density is not None:
+            raise SystemExit("--fp8 times the dense forward pass only")
+        f8 = workloads.make_fp8_inputs(inp)
+        q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q8", "k8", "v8"))
+
+        def step():                              # noqa: F811 - the FP8 step replaces the bf16 one
+            ea.fwd_fp8(q8, k8, v8, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
+                       scale=inp["scale"], stream=stream)
+
     if args.bwd:
         step()                                   # o and lse for the backward pass
         dout_bits = workloads.make_output_grad(inp, 0)
@@ -284,12 +305,13 @@ def main():
 
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
-    variant = "bwd" if args.bwd else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
+    variant = "bwd" if args.bwd else "fp8" if args.fp8 else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
     if bmask is not None:
         variant += f",block_density={args.block_density}" + (",aligned" if args.block_aligned else "")
     traffic = None if args.bwd else load_traffic(wl.key, variant)
     out = {
-        "metric": ("attention bwd" if args.bwd else "attention fwd" if bmask is None else "block-sparse attention fwd")
+        "metric": ("attention bwd" if args.bwd else "attention fwd (FP8 E4M3 inputs)" if args.fp8
+                   else "attention fwd" if bmask is None else "block-sparse attention fwd")
                   + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
@@ -300,7 +322,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3" if args.fp8 else "bf16",
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": wl.key, "B": wl.B, "H": H, "N": inp["N"], "T": T,
@@ -311,6 +333,10 @@ def main():
                      "traffic": traffic, "kernel_ms": round(ev_ms, 4),
                      "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
     }
+    if args.fp8:
+        out["roofline"]["peak"] = PEAK_FP8_TFLOPS
+        out["roofline"]["frac"] = round(achieved / PEAK_FP8_TFLOPS, 4)
+        out["roofline"]["compulsory_bytes"] = T * H * (2 * wl.d_qk + wl.d_v + 2 * wl.d_v + 4)
     if bmask is not None:
         out["config"]["kept_blocks"] = round(float(bmask.mean()), 4)
     if args.bwd:
@@ -329,7 +355,7 @@ def main():
                         "wave_tiles": tiles, "work_items": items}
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None, bmask)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None, bmask, f8)
     print(json.dumps(out), flush=True)
 
 

@@ -15,10 +15,10 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "lib", "fwd", "fwd_raw", "bwd", "bwd_raw", "debug_exp2", "strerror", "version", "geometry",
+    "AttnError", "lib", "fwd", "fwd_raw", "fwd_fp8", "fwd_fp8_raw", "bwd", "bwd_raw", "debug_exp2", "strerror", "version", "geometry",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
     "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
-    "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "LIB_PATH",
+    "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "FP8_SUPPORTED_DIMS", "LIB_PATH",
 ]
 
 # EXACT_ATTENTION_57_AMD_LIB may point at another build of the same library
@@ -37,6 +37,7 @@ SCHEDULE_LONGEST_FIRST = 0
 SCHEDULE_NATURAL = 1
 SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
 BWD_SUPPORTED_DIMS = ((64, 64), (128, 128))
+FP8_SUPPORTED_DIMS = ((128, 128),)
 
 
 class AttnError(RuntimeError):
@@ -88,6 +89,8 @@ def _load():
     L.attn_fwd_ex.restype = i32
     L.attn_fwd_opts_default.argtypes = [ctypes.POINTER(FwdOpts)]
     L.attn_fwd_opts_default.restype = None
+    L.attn_fwd_fp8.argtypes = fwd_args[:12] + [f32, f32, f32, i32, vp]
+    L.attn_fwd_fp8.restype = i32
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_bwd.restype = i32
     L.attn_strerror.argtypes = [i32]
@@ -142,23 +145,9 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
-        scale=None, rescale_threshold_log2=8.0, poly_exp_sixteenths=0,
-        schedule=SCHEDULE_LONGEST_FIRST, stats=None, block_mask=None, stream=None):
-    """Fused attention forward on torch tensors.
-
-    Fixed length: q, k [B, N, H, d_qk], v [B, N, H, d_v] (or [T, H, d] with
-    ``cu_seqlens=None`` and ``max_seqlen`` = N, T = B*N).  Packed: q, k
-    [T, H, d_qk], v [T, H, d_v] with ``cu_seqlens`` (int32 device [B+1]) and
-    ``max_seqlen`` (>= longest sequence).  bf16, contiguous, on the GPU.
-
-    Returns (o, lse): o bf16 shaped like v, lse fp32 [H, T].  Outputs are
-    allocated with torch when not given.  ``stats``: optional uint64/int64
-    device tensor of 4 counters that the kernel adds to.  ``block_mask``:
-    optional uint8/bool device tensor [B, H, nb, nb], nb = ceil(N / 128), for
-    block-sparse attention (see attn_fwd_opts in include/attn.h).
-    """
-    import torch
+def _fwd_shape(q, cu_seqlens, max_seqlen):
+    """(B, N, H, T, d_qk) of a forward call's q: [B, N, H, d] fixed length, or
+    [T, H, d] with max_seqlen (fixed length, T = B * N) or with cu_seqlens."""
     if q.dim() == 4:
         B, N, H, d_qk = q.shape
         if cu_seqlens is not None:
@@ -181,6 +170,27 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
             N = int(max_seqlen)
     else:
         raise ValueError("q must be [B, N, H, d] or [T, H, d]")
+    return B, N, H, T, d_qk
+
+
+def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
+        scale=None, rescale_threshold_log2=8.0, poly_exp_sixteenths=0,
+        schedule=SCHEDULE_LONGEST_FIRST, stats=None, block_mask=None, stream=None):
+    """Fused attention forward on torch tensors.
+
+    Fixed length: q, k [B, N, H, d_qk], v [B, N, H, d_v] (or [T, H, d] with
+    ``cu_seqlens=None`` and ``max_seqlen`` = N, T = B*N).  Packed: q, k
+    [T, H, d_qk], v [T, H, d_v] with ``cu_seqlens`` (int32 device [B+1]) and
+    ``max_seqlen`` (>= longest sequence).  bf16, contiguous, on the GPU.
+
+    Returns (o, lse): o bf16 shaped like v, lse fp32 [H, T].  Outputs are
+    allocated with torch when not given.  ``stats``: optional uint64/int64
+    device tensor of 4 counters that the kernel adds to.  ``block_mask``:
+    optional uint8/bool device tensor [B, H, nb, nb], nb = ceil(N / 128), for
+    block-sparse attention (see attn_fwd_opts in include/attn.h).
+    """
+    import torch
+    B, N, H, T, d_qk = _fwd_shape(q, cu_seqlens, max_seqlen)
     d_v = v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
@@ -208,6 +218,44 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
                  B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), opts)
     if st != ATTN_OK:
         raise AttnError(st)
+    return o, lse
+
+
+def fwd_fp8_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, B, H, N, d_qk, d_v, scale,
+                q_descale, k_descale, v_descale, causal, stream) -> int:
+    """Call attn_fwd_fp8 with raw integer pointers; returns the status code."""
+    return int(lib.attn_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
+                                int(d_qk), int(d_v), float(scale), float(q_descale), float(k_descale),
+                                float(v_descale), int(bool(causal)), stream))
+
+
+def fwd_fp8(q8, k8, v8, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
+            scale=None, q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None):
+    """FP8 attention forward: q8, k8, v8 hold OCP E4M3 values (torch.float8_e4m3fn
+    or uint8 bit patterns), contiguous CUDA tensors shaped as for ``fwd``, each
+    multiplied by its descale factor.  Returns (o bf16 shaped like v8, lse fp32
+    [H, T]); see attn_fwd_fp8 in include/attn.h."""
+    import torch
+    B, N, H, T, d_qk = _fwd_shape(q8, cu_seqlens, max_seqlen)
+    d_v = v8.shape[-1]
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous float8_e4m3fn/uint8 CUDA tensor")
+    if k8.shape != q8.shape or v8.shape[:-1] != q8.shape[:-1]:
+        raise ValueError("q8, k8, v8 shapes disagree")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    if o is None:
+        o = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q8.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    st = fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                     B, H, N, d_qk, d_v, scale, q_descale, k_descale, v_descale, causal, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8")
     return o, lse
 
 

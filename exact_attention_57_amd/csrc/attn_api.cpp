@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -125,6 +125,53 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream) {
   return attn_fwd_ex(q, k, v, o, lse, cu_seqlens, B, H, N, d_qk, d_v, scale, causal, stream, nullptr);
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                 const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+                 float scale, float q_descale, float k_descale, float v_descale,
+                 int causal, hipStream_t stream) {
+  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
+  if (!(d_qk == 128 && d_v == 128)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  for (float f : {q_descale, k_descale, v_descale})
+    if (!isfinite(f) || !(f > 0.0f)) return ATTN_ERR_VALUE;
+  if (N == 0) return ATTN_OK;
+  if (!q8 || !k8 || !v8 || !o || !lse) return ATTN_ERR_NULL;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16)) return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return ATTN_ERR_ALIGN;
+  const int rows = attn::query_block_rows();
+  const int64_t nqb = ((int64_t)N + rows - 1) / rows;
+  if ((int64_t)H * B * nqb > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
+  // a (sequence, head) K or V range is addressed by a 32-bit buffer resource
+  if ((int64_t)N * H * d_qk > INT32_MAX) return ATTN_ERR_SHAPE;
+
+  attn::Fp8Params p;
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const uint8_t*>(v8);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_qblocks = (int)nqb;
+  const double cd = fabs((double)scale) * (double)q_descale * (double)k_descale * 1.4426950408889634;
+  float c = (float)(cd < 3.0e38 ? cd : 3.0e38);
+  if (c < 1e-30f) c = 1e-30f;
+  p.c = c;
+  p.neg_scale = scale < 0.0f ? 1 : 0;
+  p.o_scale = v_descale;
+  p.tau = 8.0f;
+  p.next_stride = 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    p.next_stride = cus;
+  const hipError_t err = attn::launch_fwd_fp8(p, d_qk, causal != 0, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -175,6 +175,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream);
 
+/* FP8 forward pass: attention of E4M3 inputs with per-tensor dequantisation
+ * factors.  The pages name FP8 as the low-precision arithmetic of the Hopper
+ * generation (ainexis.cn deep dive, background, third stage) and as a
+ * precision for later versions (wittx news "FlashAttention-4", closing
+ * section); the operation is attn_fwd's on the dequantised values
+ *     q = q_descale * q8,  k = k_descale * k8,  v = v_descale * v8,
+ * with the same online softmax and conditional rescaling (threshold 8 in
+ * log2 units).  Both matrix products run on the gfx950 FP8 matrix cores; the
+ * probabilities P (<= 256) are rounded to E4M3 (nearest even) for the second
+ * product and l is the sum of those rounded values, so O is a weighted mean of
+ * v rows with weights off by at most 2^-4 relative (2^-10 absolute below the
+ * E4M3 normal range) each, and LSE carries the same weight error.
+ *
+ * q8, k8, v8: OCP E4M3 bytes [T, H, d] (token-major, heads interleaved);
+ * o: bf16 [T, H, d]; lse: fp32 [H, T] (natural log of the scaled logits
+ * scale * q . k).  cu_seqlens, B, H, N, causal: as attn_fwd.  Supported
+ * d_qk = d_v = 128 only (else ATTN_ERR_UNSUPPORTED).  scale: any finite
+ * value; q_descale, k_descale, v_descale: finite and > 0 (else
+ * ATTN_ERR_VALUE).  Alignment: 16 bytes for q8, k8, v8, o; 4 for lse and
+ * cu_seqlens.  Ownership, streams and errors as attn_fwd. */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                 const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+                 float scale, float q_descale, float k_descale, float v_descale,
+                 int causal, hipStream_t stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int attn_version(void);
 

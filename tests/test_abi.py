@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("attn_fwd", "attn_fwd_ex", "attn_fwd_opts_default", "attn_strerror",
-                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry", "attn_bwd"):
+                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry", "attn_bwd", "attn_fwd_fp8"):
         assert want in names
 
 
@@ -169,3 +169,36 @@ def test_block_mask_validation(kw, code):
         o.poly_exp_sixteenths = kw.pop("poly")
     assert call(opts=o, **kw) == code
 
+
+
+def call_fp8(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, cu=None, B=1, H=1, N=1, d_qk=128, d_v=128,
+                scale=1.0, qd=1.0, kd=1.0, vd=1.0, causal=0, stream=None)
+    args.update(kw)
+    return ea.fwd_fp8_raw(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu"],
+                          args["B"], args["H"], args["N"], args["d_qk"], args["d_v"], args["scale"],
+                          args["qd"], args["kd"], args["vd"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), ea.ATTN_ERR_SHAPE),
+    (dict(H=0), ea.ATTN_ERR_SHAPE),
+    (dict(N=-1), ea.ATTN_ERR_SHAPE),
+    (dict(H=64, N=2 ** 18 + 1), ea.ATTN_ERR_SHAPE),
+    (dict(d_qk=64, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d_qk=192, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), ea.ATTN_ERR_VALUE),
+    (dict(qd=0.0), ea.ATTN_ERR_VALUE),
+    (dict(kd=-1.0), ea.ATTN_ERR_VALUE),
+    (dict(vd=math.inf), ea.ATTN_ERR_VALUE),
+    (dict(vd=math.nan), ea.ATTN_ERR_VALUE),
+    (dict(k=None), ea.ATTN_ERR_NULL),
+    (dict(lse=None), ea.ATTN_ERR_NULL),
+    (dict(v=P + 8), ea.ATTN_ERR_ALIGN),
+    (dict(o=P + 2), ea.ATTN_ERR_ALIGN),
+    (dict(lse=P + 2), ea.ATTN_ERR_ALIGN),
+    (dict(cu=P + 1), ea.ATTN_ERR_ALIGN),
+    (dict(N=0, q=None, k=None, v=None, o=None, lse=None), ea.ATTN_OK),
+])
+def test_fp8_validation_codes(kw, code):
+    assert call_fp8(**kw) == code
