@@ -57,7 +57,10 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk 
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "noncausal_b4h16n4096d128"
-KERNEL_SOURCES = ["exact_attention_57_amd/csrc/attn_fwd_kernel.hip"]
+KERNEL_SOURCES = {   # sources whose hash keys a stored traffic record, per kernel family
+    "bf16": ["exact_attention_57_amd/csrc/attn_fwd_kernel.hip", "exact_attention_57_amd/csrc/attn_fwd_common.h"],
+    "fp8": ["exact_attention_57_amd/csrc/attn_fwd_fp8_kernel.hip", "exact_attention_57_amd/csrc/attn_fwd_common.h"],
+}
 BWD_FLOP_FACTOR = 2.5          # backward algorithmic FLOP / forward (5 products vs 2)
 
 
@@ -95,9 +98,9 @@ def compulsory_bytes(T, H, d_qk, d_v) -> float:
     return T * H * (2 * d_qk * 2 + d_v * 2 + d_v * 2 + 4)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str = "bf16") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -105,14 +108,16 @@ def kernel_source_hash() -> str:
 
 def load_traffic(workload: str, variant: str):
     """HBM bytes per launch from profiles/traffic_<workload>.json, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    name = f"traffic_{workload}" + ("_fp8" if variant == "fp8" else "")
+    path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("variant") != variant:
+    family = "fp8" if variant == "fp8" else "bf16"
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(family) or rec.get("variant") != variant:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -308,7 +313,7 @@ def main():
     variant = "bwd" if args.bwd else "fp8" if args.fp8 else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
     if bmask is not None:
         variant += f",block_density={args.block_density}" + (",aligned" if args.block_aligned else "")
-    traffic = None if args.bwd else load_traffic(wl.key, variant)
+    traffic = None if args.bwd or bmask is not None else load_traffic(wl.key, variant)
     out = {
         "metric": ("attention bwd" if args.bwd else "attention fwd (FP8 E4M3 inputs)" if args.fp8
                    else "attention fwd" if bmask is None else "block-sparse attention fwd")

@@ -28,7 +28,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
+DMA_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip"]   # kernels with inline-asm LDS DMAs
 ARCH = "gfx950"
 
 
@@ -55,16 +56,19 @@ def _hazards():
 
 
 def kernel_asm(dma_nop: int, extra=(), cc: str = None) -> str:
-    """gfx950 assembly of the kernel source as build() compiles it."""
+    """gfx950 assembly of the kernel sources with LDS DMAs, as build() compiles them."""
     cc = cc or hipcc()
     bdir = os.path.join(PKG_DIR, "_build")
     os.makedirs(bdir, exist_ok=True)
-    out = os.path.join(bdir, f"attn_fwd_kernel_nop{dma_nop}.s")
-    cmd = [cc, *compile_flags(extra), f"-DATTN_DMA_NOP={dma_nop}", "-x", "hip", "--cuda-device-only", "-S",
-           os.path.join(CSRC, "attn_fwd_kernel.hip"), "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True)
-    with open(out) as f:
-        return f.read()
+    text = []
+    for src in DMA_SOURCES:
+        out = os.path.join(bdir, f"{os.path.splitext(src)[0]}_nop{dma_nop}.s")
+        cmd = [cc, *compile_flags(extra), f"-DATTN_DMA_NOP={dma_nop}", "-x", "hip", "--cuda-device-only", "-S",
+               os.path.join(CSRC, src), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        with open(out) as f:
+            text.append(f.read())
+    return "\n".join(text)
 
 
 def choose_dma_nop(extra=(), cc: str = None, verbose: bool = False) -> int:

@@ -47,99 +47,9 @@
 #include <stdint.h>
 
 #include "attn_fwd_kernel.h"
-
-#ifndef ATTN_DMA_NOP
-#define ATTN_DMA_NOP 4   // s_nop operand in front of each LDS DMA (4: five wait states)
-#endif
-#define ATTN_STR2(x) #x
-#define ATTN_STR(x) ATTN_STR2(x)
-#ifndef ATTN_PREFETCH
-#define ATTN_PREFETCH 4  // matrix-phase LDS operands read ahead of their MFMA
-#endif
-#ifndef ATTN_SETPRIO
-#define ATTN_SETPRIO 1  // issue priority of the wave in its matrix phase (0: no change)
-#endif
+#include "attn_fwd_common.h"
 
 namespace attn {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
-
-// Cubic p(r) = 1 + C1 r + C2 r^2 + C3 r^3 minimising max |p(r)/2^r - 1| on
-// [0, 1] (relative minimax, max error 8.56e-5), rounded to fp32.  Derived by
-// gen_exp2_coeffs.py in this directory (a linear program on a dense grid).
-constexpr float kExp2C1 = 0x1.63e66ap-1f;   // 0.695117295
-constexpr float kExp2C2 = 0x1.d236c6p-3f;   // 0.227643535
-constexpr float kExp2C3 = 0x1.3babb0p-4f;   // 0.0770680308
-
-constexpr int kWave = 64;
-constexpr int kWaves = 8;              // two per SIMD: one per ping-pong group
-constexpr int kThreads = kWave * kWaves;
-constexpr int kRowsPerWave = 32;
-constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
-// Keys per tile: 128 where the registers allow it (d_qk <= 128), else 64
-// (96 also fits at d_qk = 192 but measured slower).
-// Larger tiles halve the per-tile cost of the phase barriers and the
-// softmax's row-wide steps.
-#ifndef ATTN_BLOCK_N_SMALL_D
-#define ATTN_BLOCK_N_SMALL_D 128
-#endif
-#ifndef ATTN_BLOCK_N_LARGE_D
-#define ATTN_BLOCK_N_LARGE_D 64
-#endif
-constexpr int block_n(int d_qk) { return d_qk <= 128 ? ATTN_BLOCK_N_SMALL_D : ATTN_BLOCK_N_LARGE_D; }
-constexpr int kXcds = 8;                         // MI355X: 8 XCDs, each with its own L2
-
-__device__ __forceinline__ float exp2_hw(float x) {
-  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
-}
-
-// 2^y = 2^n * p(r), n = floor(y), r = y - n in [0, 1).  y is clamped at -127
-// first so that -inf (a masked key) gives a value below 2^-126 instead of NaN;
-// such a term is under 2^-126 of the row's largest term.
-__device__ __forceinline__ float exp2_poly(float y) {
-  y = __builtin_fmaxf(y, -127.0f);
-  const float n = __builtin_floorf(y);
-  const float r = y - n;
-  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kExp2C3, r, kExp2C2), r, kExp2C1), r, 1.0f);
-  return __builtin_amdgcn_ldexpf(p, (int)n);
-}
-
-// Exchange a value with the partner lane l ^ 32 and combine.  The pair
-// {a, b} returned by the swap is {x[l], x[l^32]} in some order on every lane,
-// so max and sum are exact and identical on both lanes.
-__device__ __forceinline__ float max_with_partner(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-}
-__device__ __forceinline__ float sum_with_partner(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-}
-
-// x *= a, in the register that holds x.  The O accumulators are rescaled
-// only on the rare tiles whose row max grew; writing the product back into
-// the same register keeps the allocator from copying all of O on the common
-// path that skips the multiply.  (Every MFMA that wrote x completed before
-// the barrier that precedes any rescale.)
-__device__ __forceinline__ void scale_in_place(float& x, float a) {
-  asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(a));
-}
-
-// Two fp32 values -> two bf16 (round to nearest even) in one dword, low first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 // LDS tile layouts.  Each 64-key tile is stored dense (row r = key k0 + r,
 // R = d/8 chunks of 16 bytes per row); the chunk of column block c of row r
@@ -167,21 +77,6 @@ struct VSwz {
   __device__ static int f(int r) { return (R == 16) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// Tiles are filled by the four group-0 waves, during their matrix phases.
-constexpr int kLoaders = kWaves / 2;
-constexpr int kKBufs = 3;                // K tile buffers in LDS
-constexpr int kVBufs = 2;                // V tile buffers in LDS
-
-// Smallest number p of consecutive 1 KB DMA requests (64 chunks of 16 bytes)
-// after which a loader's chunk pattern repeats: a whole number of rows of R
-// chunks that is also a multiple of the swizzle period.  Request i then uses
-// the lane offset of request i mod p, shifted by whole rows.
-constexpr int dma_period(int R, int swizzle_rows) {
-  for (int p = 1; p < 64; ++p)
-    if ((p * 64) % R == 0 && ((p * 64 / R) % swizzle_rows) == 0) return p;
-  return 64;
-}
-
 template <int DQK, int DV, int BN>
 struct TileLayout {
   static constexpr int K_ELEMS = BN * DQK;               // dense K tile
@@ -198,85 +93,6 @@ struct TileLayout {
   static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
 };
 
-// One buffer_load_dwordx4 ... lds request: copies, for every lane, the
-// 16-byte chunk at byte offset lane_off + tile_off (from the resource base) to
-// bytes 16*lane .. 16*lane+15 of the 1 KB LDS block at dst.  Offsets past the
-// resource's byte count read as zeros.
-//
-// The request is inline assembly so that the compiler does not track it: it
-// cannot tell which LDS buffer a DMA writes, and would make every later LDS
-// read of the wave wait for all DMAs in flight.  Completion is awaited
-// explicitly (dma_wait_barrier) before the barrier that precedes the tile's
-// first read.  The host compilation pass only needs the kernels' launch stubs
-// and sees an empty body.
-__device__ __forceinline__ void dma_chunk(const u32x4_t& rsrc, uint32_t lane_off, uint32_t tile_off,
-                                          lds_u16_t* dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  // s_nop ATTN_DMA_NOP: the compiler's hazard checks do not look inside
-  // inline assembly, and a VMEM instruction may read an SGPR only five wait
-  // states after a VALU instruction wrote it (v_readlane reloads of spilled
-  // SGPRs, v_readfirstlane); an LDS DMA needs one after the M0 write.  The
-  // default 4 (five wait states) is always safe; the build uses 0 only for a
-  // compilation whose assembly it has checked for both hazards.
-  asm volatile("s_nop " ATTN_STR(ATTN_DMA_NOP) "\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "{m0}"(m0), "v"(lane_off), "s"(rsrc), "s"(tile_off)
-               : "memory");
-#endif
-}
-
-// One buffer_load_dword ... lds request (4 bytes per lane into the 256-byte
-// LDS block at dst), used only to pull lines into L2.
-__device__ __forceinline__ void dma_dword(const u32x4_t& rsrc, uint32_t lane_off, lds_u16_t* dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  // the same wait states as dma_chunk
-  asm volatile("s_nop " ATTN_STR(ATTN_DMA_NOP) "\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "{m0}"(m0), "v"(lane_off), "s"(rsrc)
-               : "memory");
-#endif
-}
-
-// Buffer resource for a byte range starting at base: raw (unswizzled)
-// addressing, no stride, num_records = nbytes, so that reads at or past
-// nbytes return zeros.
-__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  u32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-  r.z = __builtin_amdgcn_readfirstlane(nbytes);
-  r.w = 0x00020000u;
-  return r;
-}
-
-// Workgroup barriers of the phase schedule.  The memory clobber keeps the
-// compiler from moving LDS accesses across them.  No LDS wait is needed
-// before a barrier: every LDS read is either consumed by an MFMA of the same
-// phase (so it has returned) or reads a buffer that is not refilled for
-// another iteration.
-__device__ __forceinline__ void barrier() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_barrier" ::: "memory");
-#endif
-}
-// Wait until at most N of this wave's DMAs are in flight, then barrier: the
-// older DMAs have landed in LDS and, once every loader has waited, are
-// visible to all waves.
-template <int N>
-__device__ __forceinline__ void dma_wait_barrier() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-#endif
-}
-__device__ __forceinline__ void dma_wait_all() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#endif
-}
-
 // Order of the matrix phase's instructions for the scheduler: per slot s the
 // LDS reads of slot s + kPrefetch (one for a score-product slot, two
 // transposing reads for an output-product slot) followed by the MFMA of
@@ -292,11 +108,6 @@ __device__ __forceinline__ void pin_matrix_schedule() {
     pin_matrix_schedule<S + 1, NS, NQK>();
   }
 }
-
-struct True { static constexpr bool value = true; };
-struct False { static constexpr bool value = false; };
-struct Grp0 { static constexpr int value = 0; };
-struct Grp1 { static constexpr int value = 1; };
 
 // Block-sparse attention (SPARSE): a byte mask over 128 x 128 (query block,
 // key block) pairs says which score blocks exist.  A workgroup's 256 query
@@ -929,443 +740,6 @@ hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int np
 hipError_t launch_exp2_debug(const float* x, float* y, int n, int use_poly, hipStream_t s) {
   const int threads = 256;
   hipLaunchKernelGGL(exp2_debug_kernel, dim3((n + threads - 1) / threads), dim3(threads), 0, s, x, y, n, use_poly);
-  return hipGetLastError();
-}
-
-// ===========================================================================
-// FP8 (OCP E4M3) forward.
-//
-// The same work decode, ping-pong phases, LDS DMA pipeline and online softmax
-// as the bf16 kernel above, with both products on the gfx950 FP8 matrix
-// instruction v_mfma_f32_32x32x64_f8f6f4 (64-deep, twice the bf16 rate):
-//
-//   S^T = K Q^T      A: 32 bytes of one key row per lane (two ds_read_b128);
-//                    B: Q^T resident in 16 VGPRs
-//   O^T += V^T P^T   A: V^T gathered by ds_read_b64_tr_b8 (four per operand);
-//                    B: the S^T accumulators after the softmax, rounded to E4M3
-//
-// plus a fifth output block whose A operand is all ones: each of its rows is
-// the running row sum l of the E4M3-rounded P, so the softmax phase has no
-// row-sum additions and O / l is a weighted mean of V rows with the weights
-// the product actually used.  P <= 2^tau <= 256 stays inside E4M3's range
-// (448).  Lane layouts (checked on the hardware): for the 32x32x64 FP8
-// product lane l holds A[l % 32][32 (l / 32) + i] and B[32 (l / 32) + i][l % 32]
-// in byte i; the transposing read hands lane i of each 16-lane group byte i%8
-// of the 8-byte chunks addressed by lanes 2r + i/8, r = 0..7, as its bytes r.
-// Method sources: as for the bf16 kernel; the FP8 precision itself is named by
-// the ainexis.cn deep dive (background, third stage: FP8 on Hopper) and the
-// wittx news (closing section: new precisions such as FP8 for later versions).
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-
-constexpr int kFp8BlockN = 128;     // keys per tile
-constexpr int kFp8Prefetch = 3;     // matrix-phase operands read ahead (MFMA slots of 64 cycles)
-constexpr uint32_t kE4m3One = 0x38383838u;   // four E4M3 1.0 bytes
-
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1 (round to nearest even)
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);          // bytes 2, 3
-  return (uint32_t)w;
-}
-__device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
-  // format codes 0/0: both operands E4M3; scale operands 0: no block scaling
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// LDS layouts of the 128-byte rows (D = 128 E4M3 values, eight 16-byte chunks):
-//  * K chunk c of row r at c ^ ((r/2) mod 8): the 16 consecutive rows of a
-//    quarter-wave ds_read_b128 land in 16 distinct 4-bank groups.
-//  * V chunk c of row r at c ^ 2 (b1(r) + 2 b3(r)) (b_i: bit i of r): the 32
-//    lanes of a half-wave ds_read_b64_tr_b8 (8 rows {0-3, 8-11} + const, two
-//    chunks, two 8-byte halves) hit 32 distinct bank pairs.
-__device__ __forceinline__ int k8_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int v8_swz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
-
-// Issue-order pin for the FP8 matrix phase: slot s's MFMA follows the LDS reads
-// of slot s + kFp8Prefetch (two for a score slot, four transposing reads for
-// an output slot, none for the all-ones block).
-template <int S, int NS, int NQK, int OB, int DB>
-__device__ __forceinline__ void pin_fp8_schedule() {
-  constexpr int kDsRead = 0x100, kMfma = 0x008;
-  if constexpr (S < NS) {
-    constexpr int T = S + kFp8Prefetch;
-    if constexpr (T < NS) {
-      constexpr int n = (T < NQK) ? 2 : (((T - NQK) % OB) < DB ? 4 : 0);
-      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, n, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    pin_fp8_schedule<S + 1, NS, NQK, OB, DB>();
-  }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_fp8_kernel(Fp8Params p) {
-  static_assert(D == 128, "FP8 kernel: d_qk = d_v = 128");
-  constexpr int BN = kFp8BlockN;
-  constexpr int KB = BN / 32;              // 32-key blocks of S^T per tile
-  constexpr int KP = BN / 64;              // 64-key steps of the output product
-  constexpr int QK_STEPS = D / 64;         // 64-deep steps of the score product
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
-  constexpr int OB = DB + 1;               // + the all-ones block (row sums)
-  constexpr int RB = D;                    // bytes per K or V row
-  constexpr int TILE = BN * RB;            // bytes per K or V tile
-  constexpr int K_ISSUES = TILE / 1024 / kLoaders;
-  constexpr int V_ISSUES = K_ISSUES;
-  constexpr int ISSUES = K_ISSUES + V_ISSUES;
-  constexpr int PERIOD = dma_period(RB / 16, 16);   // both swizzles repeat every 16 rows
-  constexpr int OFFS = K_ISSUES < PERIOD ? K_ISSUES : PERIOD;
-  constexpr int LDS_BYTES = (kKBufs + kVBufs) * TILE;
-  constexpr int OS = D + 8;                          // staged O row stride (bf16 elements)
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(kWaves * kRowsPerWave * OS * 2 <= LDS_BYTES, "O staging fits in the tile buffers");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-  lds_u8_t* const lds = (lds_u8_t*)smem;
-  auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * TILE; };
-  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + (kKBufs + i) * TILE; };
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave;
-  const int g = lane / 32;
-  const int lq = lane % 32;
-
-  // ---- work decode: the bf16 kernel's XCD-aware longest-first order
-  const int W = p.H * p.B * p.n_qblocks;
-  auto decode = [&] __device__ (int i, int& h, int& b, int& qblk) __attribute__((always_inline)) {
-    const int x = i % kXcds, slot = i / kXcds;
-    const int gi = x * (W / kXcds) + min(x, W % kXcds) + slot;
-    const int pair = gi / p.n_qblocks;
-    qblk = p.n_qblocks - 1 - (gi - pair * p.n_qblocks);
-    h = pair / p.B;
-    b = pair - h * p.B;
-  };
-  auto seq_range = [&] __device__ (int b, int& seq0, int& L) __attribute__((always_inline)) {
-    if (p.cu_seqlens) {
-      seq0 = p.cu_seqlens[b];
-      L = p.cu_seqlens[b + 1] - seq0;
-    } else {
-      seq0 = b * p.N;
-      L = p.N;
-    }
-  };
-  int h, b, qblk;
-  decode(blockIdx.x, h, b, qblk);
-  int seq0, L;
-  seq_range(b, seq0, L);
-  const int T = p.cu_seqlens ? p.cu_seqlens[p.B] : p.B * p.N;
-  const int q0 = qblk * kBlockM;
-  if (q0 >= L) return;
-  const int kend = CAUSAL ? min(L, q0 + kBlockM) : L;
-  const int ntiles = (kend + BN - 1) / BN;
-  const int H = p.H;
-  const int64_t row_elems = (int64_t)H * D;           // bytes between consecutive tokens
-  const int qw0 = q0 + kRowsPerWave * wave;
-  const int qrow = qw0 + lq;
-
-  // ---- Q^T operand: lane (g, lq) holds Q[qrow][64 ks + 32 g + i], i = 0..31
-  i32x8_t qreg[QK_STEPS];
-  {
-    const uint32_t flip = p.neg_scale ? 0x80808080u : 0u;
-    const int qr = min(qrow, L - 1);
-    const uint8_t* qp = p.q + (int64_t)(seq0 + qr) * row_elems + (int64_t)h * D + 32 * g;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-      const u32x4_t lo = *(const u32x4_t*)(qp + 64 * ks) ^ flip;
-      const u32x4_t hi = *(const u32x4_t*)(qp + 64 * ks + 16) ^ flip;
-      qreg[ks] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  }
-
-  // ---- K/V tile DMAs (keys past the sequence end read as zeros)
-  const uint32_t rowbytes = (uint32_t)row_elems;
-  const uint8_t* const k_head = p.k + (int64_t)seq0 * row_elems + (int64_t)h * D;
-  const uint8_t* const v_head = p.v + (int64_t)seq0 * row_elems + (int64_t)h * D;
-  const uint32_t kv_bytes = (uint32_t)((L - 1) * row_elems + D);
-  const u32x4_t k_rsrc = make_rsrc(k_head, kv_bytes);
-  const u32x4_t v_rsrc = make_rsrc(v_head, kv_bytes);
-  const int lw = wave % kLoaders;
-  uint32_t koff[OFFS], voff[OFFS];
-#pragma unroll
-  for (int i = 0; i < OFFS; ++i) {
-    const int slot = (lw * K_ISSUES + i) * 64 + lane;
-    const int row = slot / (RB / 16), pos = slot % (RB / 16);
-    koff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ k8_swz(row)) * 16u;
-    voff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ v8_swz(row)) * 16u;
-  }
-  const uint32_t period_bytes = (uint32_t)(PERIOD * 64 / (RB / 16)) * rowbytes;
-
-  u32x4_t pq_rsrc = {0u, 0u, 0u, 0u}, pk_rsrc = {0u, 0u, 0u, 0u};
-  bool prefetch_next = false;
-  if (p.next_stride > 0 && (int)blockIdx.x + p.next_stride < W) {
-    int h2, b2, qblk2, seq2, L2;
-    decode(blockIdx.x + p.next_stride, h2, b2, qblk2);
-    seq_range(b2, seq2, L2);
-    const int q2 = qblk2 * kBlockM;
-    if (q2 < L2) {
-      prefetch_next = true;
-      const uint32_t qrows = (uint32_t)min(kBlockM, L2 - q2), krows = (uint32_t)min(kBlockM, L2);
-      pq_rsrc = make_rsrc(p.q + (int64_t)(seq2 + q2) * row_elems + (int64_t)h2 * D, qrows * rowbytes);
-      pk_rsrc = make_rsrc(p.k + (int64_t)seq2 * row_elems + (int64_t)h2 * D, krows * rowbytes);
-    }
-  }
-  auto prefetch_l2 = [&] __device__ (lds_u8_t* garbage) __attribute__((always_inline)) {
-    const int pw = wave - kWaves / 2;                  // 0..3 in group 1: one 128-byte row per lane
-    const uint32_t off = (uint32_t)(pw * 64 + lane) * rowbytes;
-    dma_dword(pq_rsrc, off, (lds_u16_t*)garbage);
-    dma_dword(pk_rsrc, off, (lds_u16_t*)garbage);
-  };
-  auto tile_off = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
-    return t < ntiles ? (uint32_t)(t * BN) * rowbytes : kv_bytes;
-  };
-  auto dma = [&] __device__ (int d, uint32_t tk, uint32_t tv, lds_u8_t* kdst, lds_u8_t* vdst)
-      __attribute__((always_inline)) {
-    if (d < V_ISSUES) {
-      dma_chunk(v_rsrc, voff[d % PERIOD], tv + (uint32_t)(d / PERIOD) * period_bytes,
-                (lds_u16_t*)(vdst + (lw * V_ISSUES + d) * 1024));
-    } else {
-      const int e = d - V_ISSUES;
-      dma_chunk(k_rsrc, koff[e % PERIOD], tk + (uint32_t)(e / PERIOD) * period_bytes,
-                (lds_u16_t*)(kdst + (lw * K_ISSUES + e) * 1024));
-    }
-  };
-
-  // ---- LDS read addressing.  Score slot (ks, kb): K row 32 kb + lq, chunks
-  // 4 ks + 2 g and 4 ks + 2 g + 1.  Output slot (kp, db): read j = 0..3 of
-  // the V^T operand; lane s of 16-lane group G addresses key row
-  // 64 kp + 16 j + 8 (r/4) + 4 g + r%4 (r = s/2), byte column
-  // 32 db + 16 (G%2) + 8 (s%2), which hands destination lane (g, m) the keys
-  // whose P sits in the same bytes of its B operand.
-  int kread[QK_STEPS][2];
-#pragma unroll
-  for (int ks = 0; ks < QK_STEPS; ++ks)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) kread[ks][hh] = lq * RB + (((4 * ks + 2 * g + hh) ^ k8_swz(lq)) * 16);
-  int vread[DB];
-  {
-    const int G = lane / 16, s = lane % 16, r = s / 2;
-    const int row0 = 8 * (r / 4) + 4 * g + (r % 4);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vread[db] = row0 * RB + (((2 * db + (G % 2)) ^ v8_swz(row0)) * 16) + 8 * (s % 2);
-  }
-
-  // ---- per-wave state
-  f32x16_t sacc[KB];
-  float mx_raw = -__builtin_inff();
-  i32x8_t pb[KP];
-#pragma unroll
-  for (int kp = 0; kp < KP; ++kp) pb[kp] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  f32x16_t oacc[OB];
-#pragma unroll
-  for (int ob = 0; ob < OB; ++ob)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[ob][r] = 0.0f;
-  float m_run = -__builtin_inff();
-  const float c = p.c;
-  const float tau_dec =
-      __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_fmaxf(p.tau, 0.0f))));
-
-  auto row_max = [&] __device__ () __attribute__((always_inline)) -> float {
-    float mx0 = sacc[0][0], mx1 = sacc[0][1];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
-        mx0 = __builtin_fmaxf(mx0, sacc[kb][r]);
-        mx1 = __builtin_fmaxf(mx1, sacc[kb][r + 1]);
-      }
-    return max_with_partner(__builtin_fmaxf(mx0, mx1));
-  };
-
-  constexpr int NQK = QK_STEPS * KB;
-  constexpr int NS = NQK + KP * OB;
-  constexpr int kDmaStride = NS / ISSUES;
-  static_assert(kDmaStride >= 1 && kFp8Prefetch <= NQK, "matrix-phase slots");
-  const i32x8_t ones = {(int)kE4m3One, (int)kE4m3One, (int)kE4m3One, (int)kE4m3One,
-                        (int)kE4m3One, (int)kE4m3One, (int)kE4m3One, (int)kE4m3One};
-  auto read_op = [&] __device__ (int s, const lds_u8_t* vt, const lds_u8_t* kt) __attribute__((always_inline))
-      -> i32x8_t {
-    if (s < NQK) {
-      const int ks = s / KB, kb = s % KB;
-      const u32x4_t lo = *(const lds_u32x4_t*)(kt + kread[ks][0] + kb * 32 * RB);
-      const u32x4_t hi = *(const lds_u32x4_t*)(kt + kread[ks][1] + kb * 32 * RB);
-      return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    const int q = s - NQK, kp = q / OB, db = q % OB;
-    if (db == DB) return ones;
-    const lds_u8_t* vr = vt + vread[db] + 64 * kp * RB;
-    const i32x2_t r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr));
-    const i32x2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 16 * RB));
-    const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 32 * RB));
-    const i32x2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 48 * RB));
-    return i32x8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-  };
-  i32x8_t op_pre[kFp8Prefetch];
-  auto prefetch = [&] __device__ (const lds_u8_t* vt, const lds_u8_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < kFp8Prefetch; ++s) op_pre[s] = read_op(s, vt, kt);
-  };
-  auto matrix = [&] __device__ (auto dma_tag, const lds_u8_t* vt, const lds_u8_t* kt, uint32_t tk, uint32_t tv,
-                                lds_u8_t* kdst, lds_u8_t* vdst) __attribute__((always_inline)) {
-    constexpr bool DMA = decltype(dma_tag)::value;
-    i32x8_t op[NS];
-#pragma unroll
-    for (int s = 0; s < kFp8Prefetch; ++s) op[s] = op_pre[s];
-    const f32x16_t zero = {};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + kFp8Prefetch < NS) op[s + kFp8Prefetch] = read_op(s + kFp8Prefetch, vt, kt);
-      if (s < NQK) {
-        const int ks = s / KB, kb = s % KB;
-        sacc[kb] = mfma_fp8(op[s], qreg[ks], ks == 0 ? zero : sacc[kb]);
-      } else {
-        const int q = s - NQK, kp = q / OB, db = q % OB;
-        oacc[db] = mfma_fp8(op[s], pb[kp], oacc[db]);
-      }
-      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISSUES) dma(s / kDmaStride, tk, tv, kdst, vdst);
-    }
-    mx_raw = row_max();
-    asm volatile("" : "+v"(mx_raw));
-    pin_fp8_schedule<0, NS, NQK, OB, DB>();
-  };
-
-  auto needs_mask = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * BN;
-    return (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > qw0);
-  };
-  // Softmax of tile t: masks, conditional rescale of O (and of the row-sum
-  // block), P = exp2(c s - m) rounded to E4M3 into the B operands.
-  auto softmax = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * BN;
-    float mx = mx_raw;
-    if (needs_mask(t)) {
-      const int lim = CAUSAL ? min(L - 1, qrow) : (L - 1);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
-          if (key > lim) sacc[kb][r] = -__builtin_inff();
-        }
-      mx = row_max();
-    }
-    const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-    const bool need = m_tile > m_run + tau_dec;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = need ? __builtin_fmaxf(m_run, m_tile) : m_run;
-      const float alpha = need ? exp2_hw(m_run - m_new) : 1.0f;
-#pragma unroll
-      for (int ob = 0; ob < OB; ++ob)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = oacc[ob][r];
-          scale_in_place(x, alpha);
-          oacc[ob][r] = x;
-        }
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_fmaf(sacc[kb][r], c, neg_m);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_hw(sacc[kb][r]);
-    // B operand of 64-key step kp: dword w holds S^T block 2 kp + w/4,
-    // registers 4 (w%4) .. 4 (w%4) + 3
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb = 2 * kp + w / 4, r = 4 * (w % 4);
-        pb[kp][w] = (int)pack_e4m3x4(sacc[kb][r], sacc[kb][r + 1], sacc[kb][r + 2], sacc[kb][r + 3]);
-      }
-  };
-
-  auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
-    constexpr int G = decltype(grp_tag)::value;
-    int b0 = 0;
-    if (G == 0) prefetch(vbuf(1), kbuf(0));
-    for (int j = 0; j <= ntiles; ++j) {
-      const int bm1 = (b0 == 0) ? 2 : b0 - 1;
-      const int bp1 = (b0 == 2) ? 0 : b0 + 1;
-      const int vc = j & 1, vp = vc ^ 1;
-      if (G == 0) {
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
-        matrix(True{}, vbuf(vp), kbuf(b0), tile_off(j + 2), tile_off(j), kbuf(bm1), vbuf(vc));
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        dma_wait_barrier<ISSUES>();              // K[j+1] has landed
-        if (j < ntiles) softmax(j);
-        prefetch(vbuf(vc), kbuf(bp1));
-        dma_wait_barrier<K_ISSUES>();            // V[j] has landed
-      } else {
-        if (prefetch_next && j == ntiles - 1) prefetch_l2(kbuf(bm1));
-        if (j >= 1 && j - 1 < ntiles) softmax(j - 1);
-        prefetch(vbuf(vp), kbuf(b0));
-        barrier();
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
-        matrix(False{}, vbuf(vp), kbuf(b0), 0u, 0u, kbuf(bm1), vbuf(vc));
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        barrier();
-      }
-      b0 = bp1;
-    }
-  };
-  for (int i = tid; i < TILE / 16; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
-  if (wave < kWaves / 2) {
-#pragma unroll
-    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, tile_off(0), 0u, kbuf(0), vbuf(0));
-#pragma unroll
-    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, tile_off(1), 0u, kbuf(1), vbuf(0));
-  }
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#endif
-  if (wave < kWaves / 2) run(Grp0{});
-  else run(Grp1{});
-  dma_wait_all();
-
-  // ---- epilogue: O = v_descale * O^T / l (bf16), LSE = (m + log2 l) ln 2;
-  // every row of the all-ones block holds l
-  barrier();
-  const float l_tot = oacc[DB][0];
-  const float inv = p.o_scale / l_tot;
-  lds_u16_t* const ost = (lds_u16_t*)lds + wave * kRowsPerWave * OS;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x2_t w;
-      w.x = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-      w.y = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-      *(__attribute__((address_space(3))) u32x2_t*)(ost + lq * OS + db * 32 + 8 * jj + 4 * g) = w;
-    }
-  {
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;
-    const int cc = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave / RPI; ++i) {
-      const int r = i * RPI + lane / CPR;
-      const u32x4_t w = *(const lds_u32x4_t*)(ost + r * OS + cc * 8);
-      if (qw0 + r < L) *(u32x4_t*)(p.o + (int64_t)(seq0 + qw0 + r) * H * D + (int64_t)h * D + cc * 8) = w;
-    }
-  }
-  if (qrow < L && g == 0)
-    p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
-}
-
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool causal, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
-  const dim3 grid(p.H * p.B * p.n_qblocks), block(kThreads);
-  if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
