@@ -35,13 +35,22 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 constexpr int kFp8BlockN = 128;     // keys per tile
-constexpr int kFp8Prefetch = 3;     // matrix-phase operands read ahead (MFMA slots of 64 cycles)
+#ifndef ATTN_FP8_PREFETCH
+#define ATTN_FP8_PREFETCH 3
+#endif
+#ifndef ATTN_FP8_SETPRIO
+#define ATTN_FP8_SETPRIO ATTN_SETPRIO
+#endif
+constexpr int kFp8Prefetch = ATTN_FP8_PREFETCH;   // matrix-phase operands read ahead (MFMA slots of 64 cycles)
 constexpr uint32_t kE4m3One = 0x38383838u;   // four E4M3 1.0 bytes
 
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1 (round to nearest even)
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);          // bytes 2, 3
-  return (uint32_t)w;
+// Four floats -> four E4M3 bytes (round to nearest even).  The conversion
+// writes two bytes and keeps the other two of its destination; `dead` (any
+// register whose value is no longer needed) serves as that destination, so no
+// zeroing move precedes the first half.
+__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d, int dead) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, dead, false);   // bytes 0, 1
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);              // bytes 2, 3
 }
 __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
   // format codes 0/0: both operands E4M3; scale operands 0: no block scaling
@@ -358,7 +367,7 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = 2 * kp + w / 4, r = 4 * (w % 4);
-        pb[kp][w] = (int)pack_e4m3x4(sacc[kb][r], sacc[kb][r + 1], sacc[kb][r + 2], sacc[kb][r + 3]);
+        pb[kp][w] = pack_e4m3x4(sacc[kb][r], sacc[kb][r + 1], sacc[kb][r + 2], sacc[kb][r + 3], pb[kp][w]);
       }
   };
 
@@ -371,9 +380,9 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
       const int bp1 = (b0 == 2) ? 0 : b0 + 1;
       const int vc = j & 1, vp = vc ^ 1;
       if (G == 0) {
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
+        if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_FP8_SETPRIO);
         matrix(True{}, vbuf(vp), kbuf(b0), tile_off(j + 2), tile_off(j), kbuf(bm1), vbuf(vc));
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(0);
         dma_wait_barrier<ISSUES>();              // K[j+1] has landed
         if (j < ntiles) softmax(j);
         prefetch(vbuf(vc), kbuf(bp1));
@@ -383,9 +392,9 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
         if (j >= 1 && j - 1 < ntiles) softmax(j - 1);
         prefetch(vbuf(vp), kbuf(b0));
         barrier();
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
+        if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_FP8_SETPRIO);
         matrix(False{}, vbuf(vp), kbuf(b0), 0u, 0u, kbuf(bm1), vbuf(vc));
-        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(0);
         barrier();
       }
       b0 = bp1;
