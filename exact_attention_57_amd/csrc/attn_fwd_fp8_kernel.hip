@@ -66,16 +66,33 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
 __device__ __forceinline__ int k8_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
 
-// Issue-order pin for the FP8 matrix phase: slot s's MFMA follows the LDS reads
-// of slot s + kFp8Prefetch (two for a score slot, four transposing reads for
-// an output slot, none for the all-ones block).
+#ifndef ATTN_FP8_INTERLEAVE
+#define ATTN_FP8_INTERLEAVE 0
+#endif
+// Logical slot at position pos of the matrix phase (score slots 0..NQK-1,
+// output slots NQK..).  Plain order: all score slots, then the output slots.
+// Interleaved: the kFp8Prefetch score slots whose operands are read ahead,
+// then output and score slots alternating, then the remaining output slots,
+// which spreads the transposing V reads over the phase.
+template <int NQK>
+__host__ __device__ constexpr int fp8_slot_at(int pos) {
+  if (!ATTN_FP8_INTERLEAVE || pos < kFp8Prefetch) return pos;
+  const int p = pos - kFp8Prefetch, left = NQK - kFp8Prefetch;
+  if (p < 2 * left) return (p % 2 == 0) ? NQK + p / 2 : kFp8Prefetch + p / 2;
+  return NQK + left + (p - 2 * left);
+}
+
+// Issue-order pin for the FP8 matrix phase: the MFMA at position s follows the
+// LDS reads of position s + kFp8Prefetch (two for a score slot, four
+// transposing reads for an output slot, none for the all-ones block).
 template <int S, int NS, int NQK, int OB, int DB>
 __device__ __forceinline__ void pin_fp8_schedule() {
   constexpr int kDsRead = 0x100, kMfma = 0x008;
   if constexpr (S < NS) {
     constexpr int T = S + kFp8Prefetch;
     if constexpr (T < NS) {
-      constexpr int n = (T < NQK) ? 2 : (((T - NQK) % OB) < DB ? 4 : 0);
+      constexpr int L = fp8_slot_at<NQK>(T);
+      constexpr int n = (L < NQK) ? 2 : (((L - NQK) % OB) < DB ? 4 : 0);
       if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, n, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
@@ -267,6 +284,8 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   constexpr int NQK = QK_STEPS * KB;
   constexpr int NS = NQK + KP * OB;
   constexpr int kDmaStride = NS / ISSUES;
+  // the operands read ahead at the end of the previous phase are score slots
+  // (K tile, awaited before that point); V tiles are awaited later
   static_assert(kDmaStride >= 1 && kFp8Prefetch <= NQK, "matrix-phase slots");
   const i32x8_t ones = {(int)kE4m3One, (int)kE4m3One, (int)kE4m3One, (int)kE4m3One,
                         (int)kE4m3One, (int)kE4m3One, (int)kE4m3One, (int)kE4m3One};
@@ -290,7 +309,7 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   i32x8_t op_pre[kFp8Prefetch];
   auto prefetch = [&] __device__ (const lds_u8_t* vt, const lds_u8_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < kFp8Prefetch; ++s) op_pre[s] = read_op(s, vt, kt);
+    for (int s = 0; s < kFp8Prefetch; ++s) op_pre[s] = read_op(fp8_slot_at<NQK>(s), vt, kt);
   };
   auto matrix = [&] __device__ (auto dma_tag, const lds_u8_t* vt, const lds_u8_t* kt, uint32_t tk, uint32_t tv,
                                 lds_u8_t* kdst, lds_u8_t* vdst) __attribute__((always_inline)) {
@@ -301,12 +320,13 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
     const f32x16_t zero = {};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s + kFp8Prefetch < NS) op[s + kFp8Prefetch] = read_op(s + kFp8Prefetch, vt, kt);
-      if (s < NQK) {
-        const int ks = s / KB, kb = s % KB;
+      if (s + kFp8Prefetch < NS) op[s + kFp8Prefetch] = read_op(fp8_slot_at<NQK>(s + kFp8Prefetch), vt, kt);
+      const int L = fp8_slot_at<NQK>(s);
+      if (L < NQK) {
+        const int ks = L / KB, kb = L % KB;
         sacc[kb] = mfma_fp8(op[s], qreg[ks], ks == 0 ? zero : sacc[kb]);
       } else {
-        const int q = s - NQK, kp = q / OB, db = q % OB;
+        const int q = L - NQK, kp = q / OB, db = q % OB;
         oacc[db] = mfma_fp8(op[s], pb[kp], oacc[db]);
       }
       if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISSUES) dma(s / kDmaStride, tk, tv, kdst, vdst);
