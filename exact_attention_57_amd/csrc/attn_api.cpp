@@ -179,7 +179,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream) {
   if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
-  if (!((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   if (N == 0) return ATTN_OK;  // no tokens: nothing to do
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;

@@ -72,18 +72,21 @@ int block_rows() { return kBlock; }
 // LDS layouts of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
 // bytes): chunk c of row r sits at position c ^ f(r).
 //  * row layout, read 16 bytes per lane with 16 consecutive rows per
-//    quarter-wave: f(r) = r mod 16 (R = 16), (r/2) mod 8 (R = 8);
+//    quarter-wave: f(r) = r mod 16 (R = 16), (r/2) mod 8 (R = 8 or 24: two
+//    rows share a 64-bank window, or a row of 24 chunks starts on alternate
+//    halves of it);
 //  * transposed layout, read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
-//    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8).
-// Both are invariant under a shift of r by a multiple of 16.
+//    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8 or 24).
+// Both are invariant under a shift of r by a multiple of 16, and keep a chunk
+// inside its aligned group of 8, so c ^ f(r) < R.
 template <int D>
 struct RowSwz {
-  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
   __device__ static int f(int r) { return (D == 128) ? (r & 15) : ((r >> 1) & 7); }
 };
 template <int D>
 struct TrSwz {
-  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
   __device__ static int f(int r) { return (D == 128) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
@@ -126,6 +129,9 @@ __device__ __forceinline__ void decode_block(const BwdParams& p, bool reverse, i
   h = pair / p.B;
   b = pair - h * p.B;
 }
+
+template <bool V>
+struct GroupTag { static constexpr bool value = V; };
 
 // Row sigma(m): m with bits 2 and 3 swapped.
 __device__ __forceinline__ int sigma(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -184,11 +190,17 @@ __device__ __forceinline__ void tile_store(const TileRegs<D, NT>& t, lds_u16_t* 
 
 // Per-lane LDS element offsets.  Row reads (A operand, 32 rows in sigma order,
 // k-step s: 8 columns from 16 s + 8 g); transposed reads (A operand: columns
-// db*32 + (lane % 32) at 8 consecutive rows from 8 g, as two 4-row reads).
-template <int D>
+// db*32 + (lane % 32) at 8 consecutive rows from 8 g, as two 4-row reads),
+// from a tile in the transposed layout, or in the row layout when TR_ROW
+// (a tile stored once for both kinds of read: correct, with 2-way bank
+// conflicts on the transposed reads).
+template <int D, bool TR_ROW = false>
 struct Reads {
   int row[D / 16];
   int tr[D / 32];
+  // rows 4..7 of a transposed read: the transposed layout's swizzle is the
+  // same 4 rows further on, the row layout's (r/2 mod 8) is not
+  int tr_hi[TR_ROW ? D / 32 : 1];
   __device__ Reads(int lane) {
     const int g = lane / 32, sig = sigma(lane % 32);
 #pragma unroll
@@ -200,20 +212,23 @@ struct Reads {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int d = db * 32 + 16 * (lg % 2) + 4 * (sl % 4);
-      tr[db] = vrow * D + (((d / 8) ^ TrSwz<D>::f(vrow)) * 8) + (d % 8);
+      const int sw = TR_ROW ? RowSwz<D>::f(vrow) : TrSwz<D>::f(vrow);
+      tr[db] = vrow * D + (((d / 8) ^ sw) * 8) + (d % 8);
+      if constexpr (TR_ROW) tr_hi[db] = (vrow + 4) * D + (((d / 8) ^ RowSwz<D>::f(vrow + 4)) * 8) + (d % 8);
     }
   }
 };
-template <int D>
-__device__ __forceinline__ bf16x8_t read_row(const lds_u16_t* tile, const Reads<D>& rd, int s, int blk) {
+template <int D, bool TR_ROW>
+__device__ __forceinline__ bf16x8_t read_row(const lds_u16_t* tile, const Reads<D, TR_ROW>& rd, int s, int blk) {
   return *(const lds_bf16x8_t*)(tile + rd.row[s] + blk * 32 * D);
 }
 // rows r0 .. r0+15 (r0 a multiple of 16), column block db
-template <int D>
-__device__ __forceinline__ bf16x8_t read_tr(const lds_u16_t* tile, const Reads<D>& rd, int db, int r0) {
+template <int D, bool TR_ROW>
+__device__ __forceinline__ bf16x8_t read_tr(const lds_u16_t* tile, const Reads<D, TR_ROW>& rd, int db, int r0) {
   const lds_u16_t* a = tile + rd.tr[db] + r0 * D;
+  const lds_u16_t* a_hi = TR_ROW ? tile + rd.tr_hi[db] + r0 * D : a + 4 * D;
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * D));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a_hi));
   const i16x4_t both[2] = {lo, hi};
   return __builtin_bit_cast(bf16x8_t, both);
 }
@@ -249,19 +264,23 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
       *(lds_u32x2_t*)(stage + lq * OS + db * 32 + 8 * jj + 4 * g) = w;
     }
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int RPI = kWave / CPR;           // rows per store
-  const int c = lane % CPR;
+  static_assert((kRows * CPR) % kWave == 0, "whole stores");
 #pragma unroll
-  for (int i = 0; i < kRows / RPI; ++i) {
-    const int r = i * RPI + lane / CPR;
+  for (int i = 0; i < kRows * CPR / kWave; ++i) {
+    const int idx = i * kWave + lane, r = idx / CPR, c = idx % CPR;
     const u32x4_t w = *(const lds_u32x4_t*)(stage + r * OS + c * 8);
     if (r < nvalid) *(u32x4_t*)(out + (row0 + r) * (int64_t)H * D + (int64_t)h * D + c * 8) = w;
   }
 }
 
 // ---- dQ: one workgroup per block of 128 query rows of one (sequence, head).
+// Two waves per SIMD (two workgroups per CU) up to d_qk = 128; at d_qk = 192
+// the resident Q, dO and dQ accumulators need one wave's 512 registers.
+template <int DQK>
+constexpr int dq_waves_per_simd() { return DQK > 128 ? 1 : 2; }
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<DQK>(), dq_waves_per_simd<DQK>())))
 void bwd_dq_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
   constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
@@ -382,7 +401,12 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)
 void bwd_dkdv_split_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, KBLK = DQK / 32, VBLK = DV / 32, QB = kTile / 32;
   constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
-  constexpr int TILE_ELEMS = 2 * Q_ELEMS + 2 * O_ELEMS + 2 * kTile * 2;   // + LSE (log2 units), D
+  // Q is read row-wise (S) and transposed (dK); at d_qk = 192 two copies of
+  // two buffers would not fit in LDS, so the tile is stored once, in the row
+  // layout, and the transposed reads take that layout's bank conflicts
+  constexpr bool Q_ONCE = DQK > 128;
+  constexpr int QS = (Q_ONCE ? 1 : 2) * Q_ELEMS;                       // Q elements stored per tile
+  constexpr int TILE_ELEMS = QS + 2 * O_ELEMS + 2 * kTile * 2;          // + LSE (log2 units), D
   constexpr int P_ELEMS = kWaves * kWave * 16;                          // 32 x 32 bf16 per dV wave
   constexpr int STAGE_ELEMS = 2 * kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
   constexpr int WORK_ELEMS = 2 * TILE_ELEMS + 2 * P_ELEMS;
@@ -406,12 +430,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   const int key = kw0 + lq;
   const bool key_valid = key < L;
 
-  // dV group: K rows of its keys (B operand of S); dK group: V rows (of dP)
-  bf16x8_t breg[(QK_STEPS > V_STEPS) ? QK_STEPS : V_STEPS];
-  if (kgrp) load_b_operand<DV>(*(bf16x8_t(*)[V_STEPS])breg, p.v, seq0 + key, p.H, h, g, key_valid);
-  else load_b_operand<DQK>(*(bf16x8_t(*)[QK_STEPS])breg, p.k, seq0 + key, p.H, h, g, key_valid);
 
-  const Reads<DQK> rq(lane);
+  const Reads<DQK, Q_ONCE> rq(lane);
   const Reads<DV> ro(lane);
   const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
   const int ntiles = (L - qstart + kTile - 1) / kTile;
@@ -423,10 +443,6 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   const float* const lse_h = p.lse + (int64_t)h * T + seq0;
   const float* const d_h = p.delta + (int64_t)h * T + seq0;
 
-  constexpr int ABLK = KBLK > VBLK ? KBLK : VBLK;
-  f32x16_t acc[ABLK];                        // dK^T blocks (dK group) or dV^T blocks (dV group)
-#pragma unroll
-  for (int i = 0; i < ABLK; ++i) acc[i] = f32x16_t{};
   const f32x16_t zero = {};
 
   TileRegs<DQK, kThreads2> qr;
@@ -442,141 +458,169 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
   auto stage_tile = [&] __device__ (int t) __attribute__((always_inline)) {
     lds_u16_t* const base = buf(t);
-    tile_store<DQK, true, true, kThreads2>(qr, base, base + Q_ELEMS, tid);
-    tile_store<DV, true, true, kThreads2>(dr, base + 2 * Q_ELEMS, base + 2 * Q_ELEMS + O_ELEMS, tid);
-    if (tid < 2 * kTile) ((lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS))[tid] = rowval;
+    tile_store<DQK, true, !Q_ONCE, kThreads2>(qr, base, base + Q_ELEMS, tid);
+    tile_store<DV, true, true, kThreads2>(dr, base + QS, base + QS + O_ELEMS, tid);
+    if (tid < 2 * kTile) ((lds_f32_t*)(base + QS + 2 * O_ELEMS))[tid] = rowval;
   };
   // this lane's 32 bytes of the P block of key slice wv, buffer i
   auto pslot = [&] __device__ (int i) __attribute__((always_inline)) {
     return (lds_u32x4_t*)(lds + 2 * TILE_ELEMS + i * P_ELEMS + (wv * kWave + lane) * 16);
   };
 
-  // carried from a block's first half to its second, in the same registers:
-  // the dK group's dP (16 floats) or the dV group's P (8 dwords of bf16 pairs)
-  f32x16_t carry = zero;
-  // first half of block nb: dV group S, P -> LDS; dK group dP
-  auto half_a = [&] __device__ (int nb) __attribute__((always_inline)) {
-    const int t = nb / QB, qb = nb % QB;
-    const lds_u16_t* const base = buf(t);
-    if (!kgrp) {
-      bf16x8_t a_s[QK_STEPS];
+  // Each group runs the same loop (and the same barriers) with its own
+  // registers: the group is a compile-time parameter, so the dV group's
+  // K operands and the dK group's six dK blocks are never allocated together.
+  auto group_body = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
+    constexpr bool KG = decltype(grp_tag)::value;     // dK group
+    // dV group: K rows of its keys (B operand of S); dK group: V rows (of dP)
+    constexpr int BSTEPS = KG ? V_STEPS : QK_STEPS;
+    bf16x8_t breg[BSTEPS];
+    if constexpr (KG) load_b_operand<DV>(breg, p.v, seq0 + key, p.H, h, g, key_valid);
+    else load_b_operand<DQK>(breg, p.k, seq0 + key, p.H, h, g, key_valid);
+    constexpr int ABLK = KG ? KBLK : VBLK;
+    f32x16_t acc[ABLK];                      // dK^T blocks (dK group) or dV^T blocks (dV group)
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(base, rq, ks, qb);
-      f32x16_t s = zero;
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], breg[ks], s, 0, 0, 0);
-      const lds_f32_t* const lse_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS);
-      const int q0t = qstart + t * kTile;
-      const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-        x[r] = __builtin_fmaf(s[r], p.c, -lse_s[qi]);
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = q0t + qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
-          if (!(key_valid && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
-        }
-      }
-      uint32_t pw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * i]), __builtin_amdgcn_exp2f(x[2 * i + 1]));
-        carry[i] = __uint_as_float(pw[i]);
-      }
-      lds_u32x4_t* const slot = pslot(nb & 1);
-      slot[0] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
-      slot[1] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
-    } else {
-      bf16x8_t a_p[V_STEPS];
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + 2 * Q_ELEMS, ro, vs, qb);
-      carry = zero;
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs)
-        carry = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], breg[vs], carry, 0, 0, 0);
-    }
-  };
-  // second half of block nb: dV group dV; dK group P from LDS, dS, dK
-  auto half_b = [&] __device__ (int nb) __attribute__((always_inline)) {
-    const int t = nb / QB, qb = nb % QB;
-    const lds_u16_t* const base = buf(t);
-    if (!kgrp) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t pw[4] = {__float_as_uint(carry[4 * hh]), __float_as_uint(carry[4 * hh + 1]),
-                                __float_as_uint(carry[4 * hh + 2]), __float_as_uint(carry[4 * hh + 3])};
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw);
-        bf16x8_t a_v[VBLK];
-#pragma unroll
-        for (int db = 0; db < VBLK; ++db) a_v[db] = read_tr<DV>(base + 2 * Q_ELEMS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
-#pragma unroll
-        for (int db = 0; db < VBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[db], bop, acc[db], 0, 0, 0);
-      }
-    } else {
-      const lds_f32_t* const d_s = (const lds_f32_t*)(base + 2 * Q_ELEMS + 2 * O_ELEMS) + kTile;
-      const lds_u32x4_t* const slot = pslot(nb & 1);
-      const u32x4_t praw[2] = {slot[0], slot[1]};
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t dsb[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 8 * hh + 2 * jj;
-          const int qi = qb * 32 + 16 * hh + 8 * g + 2 * jj;
-          const uint32_t w = praw[hh][jj];
-          dsb[jj] = pack_bf16x2(bf16_lo(w) * (carry[r] - d_s[qi]), bf16_hi(w) * (carry[r + 1] - d_s[qi + 1]));
-        }
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
-        bf16x8_t a_k[KBLK];
-#pragma unroll
-        for (int db = 0; db < KBLK; ++db) a_k[db] = read_tr<DQK>(base + Q_ELEMS, rq, db, qb * 32 + 16 * hh);
-#pragma unroll
-        for (int db = 0; db < KBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[db], bop, acc[db], 0, 0, 0);
-      }
-    }
-  };
+    for (int i = 0; i < ABLK; ++i) acc[i] = f32x16_t{};
 
-  // Tiles: both buffers filled up front; tile u+1 goes into the buffer of tile
-  // u-1 after barrier 2u (u >= 1), when every wave has finished block 2u-1,
-  // and is visible from barrier 2u+1 on, before block 2u+2 reads it.
-  load_tile(0);
-  stage_tile(0);
-  if (ntiles > 1) {
-    load_tile(1);
-    stage_tile(1);
-  }
-  if (ntiles > 2) load_tile(2);
-  __syncthreads();
-  half_a(0);
-  for (int nb = 0; nb < nblk; ++nb) {
-    __syncthreads();
-    if (nb % QB == 0 && nb >= QB) {
-      const int u = nb / QB;
-      if (u + 1 < ntiles) {
-        stage_tile(u + 1);
-        if (u + 2 < ntiles) load_tile(u + 2);
+    // carried from a block's first half to its second, in the same registers:
+    // the dK group's dP (16 floats) or the dV group's P (8 dwords of bf16 pairs)
+    f32x16_t carry = zero;
+    // first half of block nb: dV group S, P -> LDS; dK group dP
+    auto half_a = [&] __device__ (int nb) __attribute__((always_inline)) {
+      const int t = nb / QB, qb = nb % QB;
+      const lds_u16_t* const base = buf(t);
+      if constexpr (!KG) {
+        // operands read in groups of at most 8 k-steps (12 at d_qk = 192 would
+        // not fit beside the accumulators)
+        constexpr int CH = QK_STEPS > 8 ? QK_STEPS / 2 : QK_STEPS;
+        f32x16_t s = zero;
+  #pragma unroll
+        for (int k0 = 0; k0 < QK_STEPS; k0 += CH) {
+          bf16x8_t a_s[CH];
+  #pragma unroll
+          for (int i = 0; i < CH; ++i) a_s[i] = read_row<DQK>(base, rq, k0 + i, qb);
+  #pragma unroll
+          for (int i = 0; i < CH; ++i) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[i], breg[k0 + i], s, 0, 0, 0);
+        }
+        const lds_f32_t* const lse_s = (const lds_f32_t*)(base + QS + 2 * O_ELEMS);
+        const int q0t = qstart + t * kTile;
+        const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
+        float x[16];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+          x[r] = __builtin_fmaf(s[r], p.c, -lse_s[qi]);
+        }
+        if (masked) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int query = q0t + qb * 32 + 16 * (r / 8) + 8 * g + (r % 8);
+            if (!(key_valid && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
+          }
+        }
+        uint32_t pw[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * i]), __builtin_amdgcn_exp2f(x[2 * i + 1]));
+          carry[i] = __uint_as_float(pw[i]);
+        }
+        lds_u32x4_t* const slot = pslot(nb & 1);
+        slot[0] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+        slot[1] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
+      } else {
+        bf16x8_t a_p[V_STEPS];
+  #pragma unroll
+        for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + QS, ro, vs, qb);
+        carry = zero;
+  #pragma unroll
+        for (int vs = 0; vs < V_STEPS; ++vs)
+          carry = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], breg[vs], carry, 0, 0, 0);
       }
+    };
+    // second half of block nb: dV group dV; dK group P from LDS, dS, dK
+    auto half_b = [&] __device__ (int nb) __attribute__((always_inline)) {
+      const int t = nb / QB, qb = nb % QB;
+      const lds_u16_t* const base = buf(t);
+      if constexpr (!KG) {
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t pw[4] = {__float_as_uint(carry[4 * hh]), __float_as_uint(carry[4 * hh + 1]),
+                                  __float_as_uint(carry[4 * hh + 2]), __float_as_uint(carry[4 * hh + 3])};
+          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw);
+          bf16x8_t a_v[VBLK];
+  #pragma unroll
+          for (int db = 0; db < VBLK; ++db) a_v[db] = read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+  #pragma unroll
+          for (int db = 0; db < VBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[db], bop, acc[db], 0, 0, 0);
+        }
+      } else {
+        const lds_f32_t* const d_s = (const lds_f32_t*)(base + QS + 2 * O_ELEMS) + kTile;
+        const lds_u32x4_t* const slot = pslot(nb & 1);
+        const u32x4_t praw[2] = {slot[0], slot[1]};
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t dsb[4];
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 8 * hh + 2 * jj;
+            const int qi = qb * 32 + 16 * hh + 8 * g + 2 * jj;
+            const uint32_t w = praw[hh][jj];
+            dsb[jj] = pack_bf16x2(bf16_lo(w) * (carry[r] - d_s[qi]), bf16_hi(w) * (carry[r + 1] - d_s[qi + 1]));
+          }
+          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
+          bf16x8_t a_k[KBLK];
+  #pragma unroll
+          for (int db = 0; db < KBLK; ++db) a_k[db] = read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh);
+  #pragma unroll
+          for (int db = 0; db < KBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[db], bop, acc[db], 0, 0, 0);
+        }
+      }
+    };
+
+    // Tiles: both buffers filled up front; tile u+1 goes into the buffer of tile
+    // u-1 after barrier 2u (u >= 1), when every wave has finished block 2u-1,
+    // and is visible from barrier 2u+1 on, before block 2u+2 reads it.  Its
+    // global loads are issued one tile ahead into registers, except at
+    // d_qk = 192 (Q_ONCE), where those registers are not available and the
+    // tile is loaded right before it is staged.
+    load_tile(0);
+    stage_tile(0);
+    if (ntiles > 1) {
+      load_tile(1);
+      stage_tile(1);
     }
-    half_b(nb);
-    if (nb + 1 < nblk) half_a(nb + 1);
-  }
-  __syncthreads();                           // the staging area overlaps the tile buffers
-  lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
-  if (kgrp) {
-    f32x16_t dk[KBLK];
-#pragma unroll
-    for (int i = 0; i < KBLK; ++i) dk[i] = acc[i];
-    store_rows<DQK>(dk, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
-  } else {
-    f32x16_t dv[VBLK];
-#pragma unroll
-    for (int i = 0; i < VBLK; ++i) dv[i] = acc[i];
-    store_rows<DV>(dv, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
-  }
+    if (!Q_ONCE && ntiles > 2) load_tile(2);
+    __syncthreads();
+    half_a(0);
+    for (int nb = 0; nb < nblk; ++nb) {
+      __syncthreads();
+      if (nb % QB == 0 && nb >= QB) {
+        const int u = nb / QB;
+        if (u + 1 < ntiles) {
+          if (Q_ONCE) load_tile(u + 1);
+          stage_tile(u + 1);
+          if (!Q_ONCE && u + 2 < ntiles) load_tile(u + 2);
+        }
+      }
+      half_b(nb);
+      if (nb + 1 < nblk) half_a(nb + 1);
+    }
+    __syncthreads();                           // the staging area overlaps the tile buffers
+    lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
+    if constexpr (KG) {
+      f32x16_t dk[KBLK];
+  #pragma unroll
+      for (int i = 0; i < KBLK; ++i) dk[i] = acc[i];
+      store_rows<DQK>(dk, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+    } else {
+      f32x16_t dv[VBLK];
+  #pragma unroll
+      for (int i = 0; i < VBLK; ++i) dv[i] = acc[i];
+      store_rows<DV>(dv, 1.0f, stage, p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+    }
+  };
+  if (kgrp) group_body(GroupTag<true>{});
+  else group_body(GroupTag<false>{});
 }
 
 template <int DQK, int DV>
@@ -598,6 +642,7 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
 hipError_t launch_bwd(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
   if (d_qk == 64 && d_v == 64) return launch_dims<64, 64>(p, causal, s);
   if (d_qk == 128 && d_v == 128) return launch_dims<128, 128>(p, causal, s);
+  if (d_qk == 192 && d_v == 128) return launch_dims<192, 128>(p, causal, s);
   return hipErrorInvalidValue;
 }
 

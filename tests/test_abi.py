@@ -138,7 +138,8 @@ def call_bwd(**kw):
     (dict(H=0), ea.ATTN_ERR_SHAPE),
     (dict(N=-1), ea.ATTN_ERR_SHAPE),
     (dict(B=2, N=2 ** 30 + 1), ea.ATTN_ERR_SHAPE),
-    (dict(d_qk=192, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d_qk=128, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
     (dict(scale=math.nan), ea.ATTN_ERR_VALUE),
     (dict(do=None), ea.ATTN_ERR_NULL),

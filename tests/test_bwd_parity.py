@@ -79,7 +79,7 @@ def test_small_workload_all_elements(causal):
     full_check(inp, causal, 0.125, "B1 H2 N256 d64")
 
 
-@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_packed_all_elements(dims, causal):
     inp = workloads.make_custom_inputs([1, 77, 300, 129], 2, dims[0], dims[1], seed=3)
@@ -141,6 +141,28 @@ def test_full_size_sampled_heads(causal):
     say(f"[bwd parity] full size {wl.key} causal={causal}")
     dq, dk, dv = gpu_fwd_bwd(inp, causal, inp["scale"], dout, False)
     heads = [0, inp["H"] - 1]
+    cu = inp["cu_seqlens"]
+    b = inp["B"] - 1
+    s, e = int(cu[b]), int(cu[b + 1])
+    one = np.array([0, e - s], dtype=np.int64)
+    rq, rk, rv, _ = oracle.attention_backward(inp["q"][s:e], inp["k"][s:e], inp["v"][s:e], dout[s:e], one,
+                                              causal, inp["scale"], heads=heads)
+    check("dq", f64(dq[s:e], heads), rq)
+    check("dk", f64(dk[s:e], heads), rk)
+    check("dv", f64(dv[s:e], heads), rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_dims_full_size_sampled_heads(causal):
+    """The split head dims of the causal (192, 128) workload (B2 H32 N8192):
+    whole (sequence, head) pairs of the last sequence, two heads, against the
+    oracle (non-causal too: the kernels serve both)."""
+    wl = workloads.workload("causal_b2h32n8192dqk192dv128")
+    inp = workloads.make_inputs(wl, seed=0)
+    dout = workloads.make_output_grad(inp, 0)
+    say(f"[bwd parity] full size {wl.key} causal={causal}")
+    dq, dk, dv = gpu_fwd_bwd(inp, causal, inp["scale"], dout, False)
+    heads = [3, inp["H"] - 1]
     cu = inp["cu_seqlens"]
     b = inp["B"] - 1
     s, e = int(cu[b]), int(cu[b + 1])
