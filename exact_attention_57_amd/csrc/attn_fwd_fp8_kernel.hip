@@ -57,14 +57,22 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// LDS layouts of the 128-byte rows (D = 128 E4M3 values, eight 16-byte chunks):
-//  * K chunk c of row r at c ^ ((r/2) mod 8): the 16 consecutive rows of a
-//    quarter-wave ds_read_b128 land in 16 distinct 4-bank groups.
-//  * V chunk c of row r at c ^ 2 (b1(r) + 2 b3(r)) (b_i: bit i of r): the 32
-//    lanes of a half-wave ds_read_b64_tr_b8 (8 rows {0-3, 8-11} + const, two
-//    chunks, two 8-byte halves) hit 32 distinct bank pairs.
-__device__ __forceinline__ int k8_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int v8_swz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+// LDS layouts of the RB-byte rows (RB = D E4M3 values, RB/16 chunks of 16 bytes):
+//  * K: the 16 consecutive rows of a quarter-wave ds_read_b128 land in 16
+//    distinct 4-bank groups with chunk c of row r at
+//       c ^ ((r/2) mod 8)     RB = 128 (two rows per 256-byte bank window)
+//       c ^ ((r/4) mod 4)     RB = 64  (four rows per window)
+//  * V: the 32 lanes of a half-wave ds_read_b64_tr_b8 (8 rows {0-3, 8-11} +
+//    const, two chunks, two 8-byte halves) hit 32 distinct bank pairs with
+//       c ^ 2 (b1(r) + 2 b3(r))  RB = 128 (b_i: bit i of r)
+//       c ^ 2 b3(r)              RB = 64
+// Every pattern repeats after 16 rows.
+template <int RB>
+__device__ __forceinline__ int k8_swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+template <int RB>
+__device__ __forceinline__ int v8_swz(int r) {
+  return RB == 128 ? 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) : 2 * ((r >> 3) & 1);
+}
 
 #ifndef ATTN_FP8_INTERLEAVE
 #define ATTN_FP8_INTERLEAVE 0
@@ -103,7 +111,7 @@ __device__ __forceinline__ void pin_fp8_schedule() {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_kernel(Fp8Params p) {
-  static_assert(D == 128, "FP8 kernel: d_qk = d_v = 128");
+  static_assert(D == 64 || D == 128, "FP8 kernel: d_qk = d_v = 64 or 128");
   constexpr int BN = kFp8BlockN;
   constexpr int KB = BN / 32;              // 32-key blocks of S^T per tile
   constexpr int KP = BN / 64;              // 64-key steps of the output product
@@ -193,8 +201,8 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   for (int i = 0; i < OFFS; ++i) {
     const int slot = (lw * K_ISSUES + i) * 64 + lane;
     const int row = slot / (RB / 16), pos = slot % (RB / 16);
-    koff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ k8_swz(row)) * 16u;
-    voff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ v8_swz(row)) * 16u;
+    koff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ k8_swz<RB>(row)) * 16u;
+    voff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ v8_swz<RB>(row)) * 16u;
   }
   const uint32_t period_bytes = (uint32_t)(PERIOD * 64 / (RB / 16)) * rowbytes;
 
@@ -243,14 +251,14 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int ks = 0; ks < QK_STEPS; ++ks)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) kread[ks][hh] = lq * RB + (((4 * ks + 2 * g + hh) ^ k8_swz(lq)) * 16);
+    for (int hh = 0; hh < 2; ++hh) kread[ks][hh] = lq * RB + (((4 * ks + 2 * g + hh) ^ k8_swz<RB>(lq)) * 16);
   int vread[DB];
   {
     const int G = lane / 16, s = lane % 16, r = s / 2;
     const int row0 = 8 * (r / 4) + 4 * g + (r % 4);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      vread[db] = row0 * RB + (((2 * db + (G % 2)) ^ v8_swz(row0)) * 16) + 8 * (s % 2);
+      vread[db] = row0 * RB + (((2 * db + (G % 2)) ^ v8_swz<RB>(row0)) * 16) + 8 * (s % 2);
   }
 
   // ---- per-wave state
@@ -464,12 +472,18 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
     p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
 }
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool causal, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_fp8_dims(const Fp8Params& p, bool causal, hipStream_t s) {
   const dim3 grid(p.H * p.B * p.n_qblocks), block(kThreads);
-  if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), grid, block, 0, s, p);
+  if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool causal, hipStream_t s) {
+  if (d == 64) return launch_fp8_dims<64>(p, causal, s);
+  if (d == 128) return launch_fp8_dims<128>(p, causal, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attn

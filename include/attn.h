@@ -191,7 +191,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * q8, k8, v8: OCP E4M3 bytes [T, H, d] (token-major, heads interleaved);
  * o: bf16 [T, H, d]; lse: fp32 [H, T] (natural log of the scaled logits
  * scale * q . k).  cu_seqlens, B, H, N, causal: as attn_fwd.  Supported
- * d_qk = d_v = 128 only (else ATTN_ERR_UNSUPPORTED).  scale: any finite
+ * d_qk = d_v = 64 or 128 (else ATTN_ERR_UNSUPPORTED).  scale: any finite
  * value; q_descale, k_descale, v_descale: finite and > 0 (else
  * ATTN_ERR_VALUE).  Alignment: 16 bytes for q8, k8, v8, o; 4 for lse and
  * cu_seqlens.  Ownership, streams and errors as attn_fwd. */

@@ -140,23 +140,25 @@ def check(f, o, lse, what, causal=None, scale=None, rows=None, heads=None, **des
     return eo, el
 
 
-def test_fp8_small_all_elements():
-    inp = workloads.make_custom_inputs([256], H=2, d_qk=128, d_v=128, seed=0)
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_small_all_elements(d):
+    inp = workloads.make_custom_inputs([256], H=2, d_qk=d, d_v=d, seed=0)
     f = fp8_inputs(inp)
-    say("case: fp8 B1 H2 N256 d128 non-causal seed 0")
+    say(f"case: fp8 B1 H2 N256 d{d} non-causal seed 0")
     o, lse = run_fp8(f)
-    check(f, o, lse, "small")
+    check(f, o, lse, f"small d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_ragged_packed_all_elements(causal):
+def test_fp8_ragged_packed_all_elements(causal, d):
     lengths = [1, 63, 64, 65, 127, 128, 129, 300, 777]
-    inp = workloads.make_custom_inputs(lengths, H=3, d_qk=128, d_v=128, seed=11)
+    inp = workloads.make_custom_inputs(lengths, H=3, d_qk=d, d_v=d, seed=11)
     inp["causal"] = causal
     f = fp8_inputs(inp, prescale=(4.0, 2.0, 8.0))
-    say(f"case: fp8 ragged packed causal={causal} prescale (4, 2, 8)")
+    say(f"case: fp8 ragged packed d={d} causal={causal} prescale (4, 2, 8)")
     o, lse = run_fp8(f)
-    check(f, o, lse, f"ragged causal={causal}")
+    check(f, o, lse, f"ragged d={d} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
