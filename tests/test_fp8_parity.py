@@ -9,16 +9,18 @@ sum l taken over the same rounded values.  With p_j the unrounded weights of a
 row (relative to the kernel's kept max m, so max_j p_j >= 1 and l >= the
 oracle's row sum relative to the true max) and p~_j the rounded ones,
 
-    |p~_j - p_j| <= 2^-4 p_j + 2^-10       (half an E4M3 step; 2^-10 absolute
-                                            below the normal range, incl. flush)
+    |p~_j - p_j| <= 2^-4 p_j + min(p_j, 2^-10)   (half an E4M3 step: 2^-4 p in
+                                   the normal range, 2^-10 among the subnormals,
+                                   p itself where p flushes to 0)
     O - O_ref = sum_j (p~_j - p_j)(v_j - O_ref) / sum_j p~_j          (exact)
 
-so, with w_j the oracle's probabilities, n the number of visible keys and l
-the oracle's row sum sum_j exp(s_j - max s),
+and min(p_j, 2^-10) / l is largest with the true max (the kept max only scales
+p and l up), so with P_j = exp(s_j - max s) and l = sum_j P_j from the oracle,
+w_j = P_j / l, f_j = min(P_j, 2^-10) and F = sum_j f_j,
 
-    |O - O_ref| <= [2^-4 (sum_j w_j |v_j| + |O_ref|) + 2^-10 (n / l)(max_j |v_j| + |O_ref|)] / den
+    |O - O_ref| <= [2^-4 (sum_j w_j |v_j| + |O_ref|) + (sum_j f_j |v_j| + F |O_ref|) / l] / den
                    + 2^-8 |O_ref| + 2e-4 max_j |v_j|,
-    den = 1 - 2^-4 - 2^-10 n / l,
+    den = 1 - 2^-4 - F / l,
     |LSE - LSE_ref| <= -ln(den) + 1e-5,
 
 the last terms covering the bf16 output rounding (2^-9 relative) and the fp32
@@ -101,10 +103,11 @@ def bounds(f, causal, scale, rows=None, heads=None, q_descale=None, k_descale=No
             n = (pos + 1) if causal else np.full(len(sel), e - s)
             av = np.abs(v)
             vmax = np.array([av[:c].max(axis=0) for c in n]) if causal else np.broadcast_to(av.max(axis=0), Oi.shape)
-            flush = E4_ABS * n / l
-            den = 1.0 - E4_REL - flush
+            Fm = np.minimum(P, E4_ABS)                 # masked keys: P = 0
+            F = Fm.sum(axis=1)
+            den = 1.0 - E4_REL - F / l
             assert np.all(den > 0.5)
-            bo = (E4_REL * (W @ av + np.abs(Oi)) + flush[:, None] * (vmax + np.abs(Oi))) / den[:, None]
+            bo = (E4_REL * (W @ av + np.abs(Oi)) + (Fm @ av + F[:, None] * np.abs(Oi)) / l[:, None]) / den[:, None]
             bo += 2.0 ** -8 * np.abs(Oi) + 2e-4 * vmax
             O[r0:r0 + len(sel), hi] = Oi
             L[hi, r0:r0 + len(sel)] = m + np.log(l)
@@ -178,6 +181,20 @@ def test_fp8_empty_and_single_token_sequences():
         say(f"case: fp8 empty/single sequences causal={causal}")
         o, lse = run_fp8(f, causal=causal, packed=True)
         check(f, o, lse, f"empty+single causal={causal}", causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_large_logits_exercise_rescaling(causal):
+    """Peaked rows: std-3 inputs at scale 0.3 (logits of order +-100) make the
+    kept max stale by up to 8 (P up to 256, near E4M3's 448) and most weights
+    flush below the E4M3 range."""
+    inp = workloads.make_custom_inputs([200, 130, 1000], H=2, d_qk=128, d_v=128, seed=21, std=3.0)
+    inp["causal"] = causal
+    inp["scale"] = 0.3
+    f = fp8_inputs(inp, prescale=(0.5, 0.5, 1.0))
+    say(f"case: fp8 large logits causal={causal}")
+    o, lse = run_fp8(f)
+    check(f, o, lse, f"large logits causal={causal}")
 
 
 def test_fp8_special_values():
