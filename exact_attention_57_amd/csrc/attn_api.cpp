@@ -71,7 +71,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   if (np != 0 && np != 2 && np != 4 && np != 8) return ATTN_ERR_VALUE;
   if (op.schedule != ATTN_SCHEDULE_LONGEST_FIRST && op.schedule != ATTN_SCHEDULE_NATURAL) return ATTN_ERR_VALUE;
   if (op.block_mask) {
-    if (d_qk > 128 || np != 0) return ATTN_ERR_UNSUPPORTED;     // 128-key tiles, hardware exp2
+    if (np != 0) return ATTN_ERR_UNSUPPORTED;                   // hardware exp2 only
     if (N > 32768) return ATTN_ERR_SHAPE;                       // 256 key blocks of 128
   }
   if (N == 0) return ATTN_OK;  // no tokens: nothing to do

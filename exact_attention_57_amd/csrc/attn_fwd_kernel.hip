@@ -111,9 +111,10 @@ __device__ __forceinline__ void pin_matrix_schedule() {
 
 // Block-sparse attention (SPARSE): a byte mask over 128 x 128 (query block,
 // key block) pairs says which score blocks exist.  A workgroup's 256 query
-// rows are two query blocks; it visits the union of their kept key tiles
-// (128 keys each), in order, and a wave skips the tiles its own query block
-// does not keep.  Up to 256 key blocks (N <= 32768) in four 64-bit words.
+// rows are two query blocks; it visits the key tiles of the union of their
+// kept key blocks (one 128-key tile per block, or two 64-key tiles at
+// d_qk = 192), in order, and a wave skips the tiles its own query block does
+// not keep.  Up to 256 key blocks (N <= 32768) in four 64-bit words.
 constexpr int kMaskBlock = 128;
 constexpr int kMaskWords = 4;
 constexpr int kNoTile = 1 << 20;
@@ -122,7 +123,7 @@ template <int DQK, int DV, bool CAUSAL, int NPOLY, bool SPARSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
-  static_assert(!SPARSE || (block_n(DQK) == kMaskBlock && NPOLY == 0), "block-sparse: 128-key tiles, hardware exp");
+  static_assert(!SPARSE || (kMaskBlock % block_n(DQK) == 0 && NPOLY == 0), "block-sparse: tiles inside mask blocks, hardware exp");
   constexpr int BN = block_n(DQK);               // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
   using Lay = TileLayout<DQK, DV, BN>;
@@ -197,8 +198,10 @@ void attn_fwd_kernel(FwdParams p) {
   const bool row_valid = qrow < L;
 
   // ---- block-sparse: bitmaps (scalar registers, by ballot) of the kept key
-  // tiles among the first ntiles, for the union of the workgroup's two query
-  // blocks (um) and for this wave's own block (own).  nact tiles are visited.
+  // blocks among the first nkb, for the union of the workgroup's two query
+  // blocks (um) and for this wave's own block (own).  nact tiles are visited:
+  // TPB per kept block, except past the last tile.
+  constexpr int TPB = kMaskBlock / BN;               // tiles per mask block (1 or 2)
   uint64_t um[kMaskWords] = {};
   uint64_t own0 = 0, own1 = 0, own2 = 0, own3 = 0;   // named words: no indexed array in memory
   int nact = ntiles;
@@ -206,11 +209,12 @@ void attn_fwd_kernel(FwdParams p) {
     const int nb = p.mask_blocks;
     const uint8_t* const mrows = p.block_mask + (int64_t)(b * H + h) * nb * nb;
     const int r0 = 2 * qblk, r1 = 2 * qblk + 1;
+    const int nkb = (ntiles + TPB - 1) / TPB;        // key blocks holding the first ntiles tiles
     nact = 0;
 #pragma unroll
     for (int w = 0; w < kMaskWords; ++w) {
       const int kb = 64 * w + lane;
-      const bool in = kb < ntiles;
+      const bool in = kb < nkb;
       const bool a = in && r0 < nb && mrows[(int64_t)r0 * nb + kb] != 0;
       const bool c = in && r1 < nb && mrows[(int64_t)r1 * nb + kb] != 0;
       const uint64_t ba = __builtin_amdgcn_ballot_w64(a), bc = __builtin_amdgcn_ballot_w64(c);
@@ -220,31 +224,48 @@ void attn_fwd_kernel(FwdParams p) {
       if (w == 1) own1 = mine;
       if (w == 2) own2 = mine;
       if (w == 3) own3 = mine;
-      nact += __builtin_popcountll(um[w]);
+      nact += TPB * __builtin_popcountll(um[w]);
+    }
+    // the last key block holds one tile only when ntiles is odd (TPB = 2);
+    // its word is selected in registers (a runtime index would move um to memory)
+    if constexpr (TPB == 2) {
+      const int last = nkb - 1;
+      uint64_t lastw = 0;
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) lastw = (w == last / 64) ? um[w] : lastw;
+      if ((ntiles & 1) && ((lastw >> (last % 64)) & 1ull)) nact -= 1;
     }
   }
-  // smallest kept tile above t (kNoTile if none; the identity order when dense)
+  // smallest kept key block above kb (kNoTile if none)
+  auto next_block = [&] __device__ (int kb) __attribute__((always_inline)) -> int {
+    const int first = kb + 1;
+    int res = kNoTile;
+#pragma unroll
+    for (int w = kMaskWords - 1; w >= 0; --w) {
+      const int lo = first - 64 * w;
+      uint64_t bits = um[w];
+      if (lo >= 64) bits = 0;
+      else if (lo > 0) bits &= ~0ull << lo;
+      if (bits != 0) res = 64 * w + __builtin_ctzll(bits);
+    }
+    return res;
+  };
+  // next tile to visit after t (kNoTile if none; the identity order when
+  // dense): the second tile of t's block, else the first of the next kept block
   auto next_tile = [&] __device__ (int t) __attribute__((always_inline)) -> int {
     if constexpr (!SPARSE) {
       return t + 1;
     } else {
-      const int first = t + 1;
-      int res = kNoTile;
-#pragma unroll
-      for (int w = kMaskWords - 1; w >= 0; --w) {
-        const int lo = first - 64 * w;
-        uint64_t bits = um[w];
-        if (lo >= 64) bits = 0;
-        else if (lo > 0) bits &= ~0ull << lo;
-        if (bits != 0) res = 64 * w + __builtin_ctzll(bits);
-      }
-      return res;
+      if (TPB == 2 && t >= 0 && (t & 1) == 0 && t + 1 < ntiles) return t + 1;
+      const int kb = next_block(t < 0 ? -1 : t / TPB);
+      return kb == kNoTile ? kNoTile : TPB * kb;
     }
   };
   static_assert(kMaskWords == 4, "own0..own3");
   auto own_keeps = [&] __device__ (int t) __attribute__((always_inline)) -> bool {
-    const uint64_t bits = t < 64 ? own0 : t < 128 ? own1 : t < 192 ? own2 : own3;
-    return ((bits >> (t & 63)) & 1ull) != 0;
+    const int kb = t / TPB;
+    const uint64_t bits = kb < 64 ? own0 : kb < 128 ? own1 : kb < 192 ? own2 : own3;
+    return ((bits >> (kb & 63)) & 1ull) != 0;
   };
 
   // ---- Q^T operand, resident for the whole key loop.  Lane (g, lq) holds
@@ -712,16 +733,13 @@ static hipError_t launch_poly(const FwdParams& p, int npoly, hipStream_t s) {
 
 template <int DQK, int DV>
 static hipError_t launch_dims(const FwdParams& p, bool causal, int npoly, hipStream_t s) {
-  if constexpr (block_n(DQK) == kMaskBlock) {
-    if (p.block_mask) {
-      if (npoly != 0) return hipErrorInvalidValue;
-      const dim3 grid = (p.schedule == 0) ? dim3(p.H * p.B * p.n_qblocks) : dim3(p.H, p.B, p.n_qblocks);
-      if (causal) hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, true, 0, true>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, false, 0, true>), grid, dim3(kThreads), 0, s, p);
-      return hipGetLastError();
-    }
-  } else {
-    if (p.block_mask) return hipErrorInvalidValue;
+  static_assert(kMaskBlock % block_n(DQK) == 0, "tiles inside mask blocks");
+  if (p.block_mask) {
+    if (npoly != 0) return hipErrorInvalidValue;
+    const dim3 grid = (p.schedule == 0) ? dim3(p.H * p.B * p.n_qblocks) : dim3(p.H, p.B, p.n_qblocks);
+    if (causal) hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, true, 0, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, false, 0, true>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
   }
   return causal ? launch_poly<DQK, DV, true>(p, npoly, s) : launch_poly<DQK, DV, false>(p, npoly, s);
 }

@@ -113,8 +113,8 @@ typedef struct attn_fwd_opts {
    * then attends to the keys j of kept blocks (and j <= i if causal); a query
    * with no such key gets o = 0 and lse = -inf.  Blocks past a sequence's
    * end are ignored.  Workgroups visit only the key tiles some of their rows
-   * keep.  Requires d_qk <= 128, N <= 32768 and poly_exp_sixteenths = 0
-   * (else ATTN_ERR_UNSUPPORTED / ATTN_ERR_SHAPE).  NULL (default): dense. */
+   * keep.  Requires N <= 32768 and poly_exp_sixteenths = 0 (else
+   * ATTN_ERR_SHAPE / ATTN_ERR_UNSUPPORTED).  NULL (default): dense. */
   const uint8_t* block_mask;
 } attn_fwd_opts;
 

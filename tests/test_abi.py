@@ -157,8 +157,8 @@ def test_bwd_validation_codes(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d_qk=192, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
     (dict(poly=2), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d_qk=192, d_v=128, poly=4), ea.ATTN_ERR_UNSUPPORTED),
     (dict(N=32769), ea.ATTN_ERR_SHAPE),
     (dict(N=0, q=None, k=None, v=None, o=None, lse=None), ea.ATTN_OK),
 ])

@@ -63,6 +63,15 @@ def test_packed_ragged_d64(causal):
     check(inp, causal, 0.125, mask, "packed ragged d64", packed=True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_dims_two_tiles_per_block(causal):
+    """(192, 128): 64-key tiles, two per 128-key mask block; lengths with an
+    odd tile count, so the last kept block holds a single tile."""
+    inp = workloads.make_custom_inputs([300, 1, 0, 700, 129], 2, 192, 128, seed=25)
+    mask = workloads.make_block_mask(5, 2, int(inp["N"]), 0.5, seed=5 + causal)
+    check(inp, causal, 1.0 / np.sqrt(192), mask, "packed ragged (192,128)", packed=True)
+
+
 def test_empty_query_blocks():
     """Whole query blocks with no kept key block, and a causal mask that hides
     the only kept block from some rows."""
@@ -77,10 +86,11 @@ def test_empty_query_blocks():
     check(inp, True, 0.09, mask, "empty query blocks, causal", packed=False)
 
 
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_all_ones_mask_equals_dense_bitwise(causal):
+def test_all_ones_mask_equals_dense_bitwise(causal, dims):
     torch = torch_cuda()
-    inp = workloads.make_custom_inputs([777, 1200], 4, 128, 128, seed=24)
+    inp = workloads.make_custom_inputs([777, 1200], 4, dims[0], dims[1], seed=24)
     nb = (int(inp["N"]) + 127) // 128
     mask = np.ones((2, 4, nb, nb), dtype=np.uint8)
     o1, l1 = gpu_run(inp, causal, 0.088, mask, packed=True)
