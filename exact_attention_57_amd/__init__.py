@@ -37,7 +37,7 @@ SCHEDULE_LONGEST_FIRST = 0
 SCHEDULE_NATURAL = 1
 SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
 BWD_SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
-FP8_SUPPORTED_DIMS = ((64, 64), (128, 128))
+FP8_SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
 
 
 class AttnError(RuntimeError):

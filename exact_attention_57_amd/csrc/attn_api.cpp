@@ -132,7 +132,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
                  float scale, float q_descale, float k_descale, float v_descale,
                  int causal, hipStream_t stream) {
   if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
-  if (!((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   for (float f : {q_descale, k_descale, v_descale})
     if (!isfinite(f) || !(f > 0.0f)) return ATTN_ERR_VALUE;
@@ -170,7 +170,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
     p.next_stride = cus;
-  const hipError_t err = attn::launch_fwd_fp8(p, d_qk, causal != 0, stream);
+  const hipError_t err = attn::launch_fwd_fp8(p, d_qk, d_v, causal != 0, stream);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -57,11 +57,13 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// LDS layouts of the RB-byte rows (RB = D E4M3 values, RB/16 chunks of 16 bytes):
+// LDS layouts of the RB-byte rows (RB = d E4M3 values, RB/16 chunks of 16 bytes):
 //  * K: the 16 consecutive rows of a quarter-wave ds_read_b128 land in 16
 //    distinct 4-bank groups with chunk c of row r at
 //       c ^ ((r/2) mod 8)     RB = 128 (two rows per 256-byte bank window)
-//       c ^ ((r/4) mod 4)     RB = 64  (four rows per window)
+//       c ^ ((r/4) mod 4)     RB = 64 (four rows per window) and RB = 192 (a
+//                             row starts 12 chunks on: rows r mod 4 take four
+//                             different bank quarters, the XOR the other bits)
 //  * V: the 32 lanes of a half-wave ds_read_b64_tr_b8 (8 rows {0-3, 8-11} +
 //    const, two chunks, two 8-byte halves) hit 32 distinct bank pairs with
 //       c ^ 2 (b1(r) + 2 b3(r))  RB = 128 (b_i: bit i of r)
@@ -108,32 +110,36 @@ __device__ __forceinline__ void pin_fp8_schedule() {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_kernel(Fp8Params p) {
-  static_assert(D == 64 || D == 128, "FP8 kernel: d_qk = d_v = 64 or 128");
+  static_assert((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128) || (DQK == 192 && DV == 128),
+                "FP8 kernel: (d_qk, d_v) = (64, 64), (128, 128) or (192, 128)");
   constexpr int BN = kFp8BlockN;
   constexpr int KB = BN / 32;              // 32-key blocks of S^T per tile
   constexpr int KP = BN / 64;              // 64-key steps of the output product
-  constexpr int QK_STEPS = D / 64;         // 64-deep steps of the score product
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  constexpr int QK_STEPS = DQK / 64;       // 64-deep steps of the score product
+  constexpr int DB = DV / 32;              // 32-row blocks of O^T
   constexpr int OB = DB + 1;               // + the all-ones block (row sums)
-  constexpr int RB = D;                    // bytes per K or V row
-  constexpr int TILE = BN * RB;            // bytes per K or V tile
-  constexpr int K_ISSUES = TILE / 1024 / kLoaders;
-  constexpr int V_ISSUES = K_ISSUES;
+  constexpr int RBK = DQK, RBV = DV;        // bytes per K and per V row
+  constexpr int TILE_K = BN * RBK, TILE_V = BN * RBV;
+  constexpr int K_ISSUES = TILE_K / 1024 / kLoaders;
+  constexpr int V_ISSUES = TILE_V / 1024 / kLoaders;
   constexpr int ISSUES = K_ISSUES + V_ISSUES;
-  constexpr int PERIOD = dma_period(RB / 16, 16);   // both swizzles repeat every 16 rows
-  constexpr int OFFS = K_ISSUES < PERIOD ? K_ISSUES : PERIOD;
-  constexpr int LDS_BYTES = (kKBufs + kVBufs) * TILE;
-  constexpr int OS = D + 8;                          // staged O row stride (bf16 elements)
+  static_assert(TILE_K % (1024 * kLoaders) == 0 && TILE_V % (1024 * kLoaders) == 0, "tile split");
+  constexpr int PERIOD_K = dma_period(RBK / 16, 16);   // the swizzles repeat every 16 rows
+  constexpr int PERIOD_V = dma_period(RBV / 16, 16);
+  constexpr int OFFS_K = K_ISSUES < PERIOD_K ? K_ISSUES : PERIOD_K;
+  constexpr int OFFS_V = V_ISSUES < PERIOD_V ? V_ISSUES : PERIOD_V;
+  constexpr int LDS_BYTES = kKBufs * TILE_K + kVBufs * TILE_V;
+  constexpr int OS = DV + 8;                         // staged O row stride (bf16 elements)
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(kWaves * kRowsPerWave * OS * 2 <= LDS_BYTES, "O staging fits in the tile buffers");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   lds_u8_t* const lds = (lds_u8_t*)smem;
-  auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * TILE; };
-  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + (kKBufs + i) * TILE; };
+  auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * TILE_K; };
+  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + kKBufs * TILE_K + i * TILE_V; };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -170,7 +176,8 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   const int kend = CAUSAL ? min(L, q0 + kBlockM) : L;
   const int ntiles = (kend + BN - 1) / BN;
   const int H = p.H;
-  const int64_t row_elems = (int64_t)H * D;           // bytes between consecutive tokens
+  const int64_t qk_row = (int64_t)H * DQK;            // bytes between consecutive tokens of q, k
+  const int64_t v_row = (int64_t)H * DV;              // ... of v
   const int qw0 = q0 + kRowsPerWave * wave;
   const int qrow = qw0 + lq;
 
@@ -179,7 +186,7 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   {
     const uint32_t flip = p.neg_scale ? 0x80808080u : 0u;
     const int qr = min(qrow, L - 1);
-    const uint8_t* qp = p.q + (int64_t)(seq0 + qr) * row_elems + (int64_t)h * D + 32 * g;
+    const uint8_t* qp = p.q + (int64_t)(seq0 + qr) * qk_row + (int64_t)h * DQK + 32 * g;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) {
       const u32x4_t lo = *(const u32x4_t*)(qp + 64 * ks) ^ flip;
@@ -189,22 +196,29 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
   }
 
   // ---- K/V tile DMAs (keys past the sequence end read as zeros)
-  const uint32_t rowbytes = (uint32_t)row_elems;
-  const uint8_t* const k_head = p.k + (int64_t)seq0 * row_elems + (int64_t)h * D;
-  const uint8_t* const v_head = p.v + (int64_t)seq0 * row_elems + (int64_t)h * D;
-  const uint32_t kv_bytes = (uint32_t)((L - 1) * row_elems + D);
-  const u32x4_t k_rsrc = make_rsrc(k_head, kv_bytes);
-  const u32x4_t v_rsrc = make_rsrc(v_head, kv_bytes);
+  const uint32_t k_rowbytes = (uint32_t)qk_row, v_rowbytes = (uint32_t)v_row;
+  const uint8_t* const k_head = p.k + (int64_t)seq0 * qk_row + (int64_t)h * DQK;
+  const uint8_t* const v_head = p.v + (int64_t)seq0 * v_row + (int64_t)h * DV;
+  const uint32_t k_bytes = (uint32_t)((L - 1) * qk_row + DQK);
+  const uint32_t v_bytes = (uint32_t)((L - 1) * v_row + DV);
+  const u32x4_t k_rsrc = make_rsrc(k_head, k_bytes);
+  const u32x4_t v_rsrc = make_rsrc(v_head, v_bytes);
   const int lw = wave % kLoaders;
-  uint32_t koff[OFFS], voff[OFFS];
+  uint32_t koff[OFFS_K], voff[OFFS_V];
 #pragma unroll
-  for (int i = 0; i < OFFS; ++i) {
+  for (int i = 0; i < OFFS_K; ++i) {
     const int slot = (lw * K_ISSUES + i) * 64 + lane;
-    const int row = slot / (RB / 16), pos = slot % (RB / 16);
-    koff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ k8_swz<RB>(row)) * 16u;
-    voff[i] = (uint32_t)row * rowbytes + (uint32_t)(pos ^ v8_swz<RB>(row)) * 16u;
+    const int row = slot / (RBK / 16), pos = slot % (RBK / 16);
+    koff[i] = (uint32_t)row * k_rowbytes + (uint32_t)(pos ^ k8_swz<RBK>(row)) * 16u;
   }
-  const uint32_t period_bytes = (uint32_t)(PERIOD * 64 / (RB / 16)) * rowbytes;
+#pragma unroll
+  for (int i = 0; i < OFFS_V; ++i) {
+    const int slot = (lw * V_ISSUES + i) * 64 + lane;
+    const int row = slot / (RBV / 16), pos = slot % (RBV / 16);
+    voff[i] = (uint32_t)row * v_rowbytes + (uint32_t)(pos ^ v8_swz<RBV>(row)) * 16u;
+  }
+  const uint32_t k_period_bytes = (uint32_t)(PERIOD_K * 64 / (RBK / 16)) * k_rowbytes;
+  const uint32_t v_period_bytes = (uint32_t)(PERIOD_V * 64 / (RBV / 16)) * v_rowbytes;
 
   u32x4_t pq_rsrc = {0u, 0u, 0u, 0u}, pk_rsrc = {0u, 0u, 0u, 0u};
   bool prefetch_next = false;
@@ -216,27 +230,30 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
     if (q2 < L2) {
       prefetch_next = true;
       const uint32_t qrows = (uint32_t)min(kBlockM, L2 - q2), krows = (uint32_t)min(kBlockM, L2);
-      pq_rsrc = make_rsrc(p.q + (int64_t)(seq2 + q2) * row_elems + (int64_t)h2 * D, qrows * rowbytes);
-      pk_rsrc = make_rsrc(p.k + (int64_t)seq2 * row_elems + (int64_t)h2 * D, krows * rowbytes);
+      pq_rsrc = make_rsrc(p.q + (int64_t)(seq2 + q2) * qk_row + (int64_t)h2 * DQK, qrows * k_rowbytes);
+      pk_rsrc = make_rsrc(p.k + (int64_t)seq2 * qk_row + (int64_t)h2 * DQK, krows * k_rowbytes);
     }
   }
   auto prefetch_l2 = [&] __device__ (lds_u8_t* garbage) __attribute__((always_inline)) {
     const int pw = wave - kWaves / 2;                  // 0..3 in group 1: one 128-byte row per lane
-    const uint32_t off = (uint32_t)(pw * 64 + lane) * rowbytes;
+    const uint32_t off = (uint32_t)(pw * 64 + lane) * k_rowbytes;
     dma_dword(pq_rsrc, off, (lds_u16_t*)garbage);
     dma_dword(pk_rsrc, off, (lds_u16_t*)garbage);
   };
-  auto tile_off = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
-    return t < ntiles ? (uint32_t)(t * BN) * rowbytes : kv_bytes;
+  auto k_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BN) * k_rowbytes : k_bytes;
+  };
+  auto v_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BN) * v_rowbytes : v_bytes;
   };
   auto dma = [&] __device__ (int d, uint32_t tk, uint32_t tv, lds_u8_t* kdst, lds_u8_t* vdst)
       __attribute__((always_inline)) {
     if (d < V_ISSUES) {
-      dma_chunk(v_rsrc, voff[d % PERIOD], tv + (uint32_t)(d / PERIOD) * period_bytes,
+      dma_chunk(v_rsrc, voff[d % PERIOD_V], tv + (uint32_t)(d / PERIOD_V) * v_period_bytes,
                 (lds_u16_t*)(vdst + (lw * V_ISSUES + d) * 1024));
     } else {
       const int e = d - V_ISSUES;
-      dma_chunk(k_rsrc, koff[e % PERIOD], tk + (uint32_t)(e / PERIOD) * period_bytes,
+      dma_chunk(k_rsrc, koff[e % PERIOD_K], tk + (uint32_t)(e / PERIOD_K) * k_period_bytes,
                 (lds_u16_t*)(kdst + (lw * K_ISSUES + e) * 1024));
     }
   };
@@ -251,14 +268,14 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int ks = 0; ks < QK_STEPS; ++ks)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) kread[ks][hh] = lq * RB + (((4 * ks + 2 * g + hh) ^ k8_swz<RB>(lq)) * 16);
+    for (int hh = 0; hh < 2; ++hh) kread[ks][hh] = lq * RBK + (((4 * ks + 2 * g + hh) ^ k8_swz<RBK>(lq)) * 16);
   int vread[DB];
   {
     const int G = lane / 16, s = lane % 16, r = s / 2;
     const int row0 = 8 * (r / 4) + 4 * g + (r % 4);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      vread[db] = row0 * RB + (((2 * db + (G % 2)) ^ v8_swz<RB>(row0)) * 16) + 8 * (s % 2);
+      vread[db] = row0 * RBV + (((2 * db + (G % 2)) ^ v8_swz<RBV>(row0)) * 16) + 8 * (s % 2);
   }
 
   // ---- per-wave state
@@ -301,17 +318,17 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
       -> i32x8_t {
     if (s < NQK) {
       const int ks = s / KB, kb = s % KB;
-      const u32x4_t lo = *(const lds_u32x4_t*)(kt + kread[ks][0] + kb * 32 * RB);
-      const u32x4_t hi = *(const lds_u32x4_t*)(kt + kread[ks][1] + kb * 32 * RB);
+      const u32x4_t lo = *(const lds_u32x4_t*)(kt + kread[ks][0] + kb * 32 * RBK);
+      const u32x4_t hi = *(const lds_u32x4_t*)(kt + kread[ks][1] + kb * 32 * RBK);
       return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
     const int q = s - NQK, kp = q / OB, db = q % OB;
     if (db == DB) return ones;
-    const lds_u8_t* vr = vt + vread[db] + 64 * kp * RB;
+    const lds_u8_t* vr = vt + vread[db] + 64 * kp * RBV;
     const i32x2_t r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr));
-    const i32x2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 16 * RB));
-    const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 32 * RB));
-    const i32x2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 48 * RB));
+    const i32x2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 16 * RBV));
+    const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 32 * RBV));
+    const i32x2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vr + 48 * RBV));
     return i32x8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
   };
   i32x8_t op_pre[kFp8Prefetch];
@@ -409,7 +426,7 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
       const int vc = j & 1, vp = vc ^ 1;
       if (G == 0) {
         if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_FP8_SETPRIO);
-        matrix(True{}, vbuf(vp), kbuf(b0), tile_off(j + 2), tile_off(j), kbuf(bm1), vbuf(vc));
+        matrix(True{}, vbuf(vp), kbuf(b0), k_tile(j + 2), v_tile(j), kbuf(bm1), vbuf(vc));
         if (ATTN_FP8_SETPRIO) __builtin_amdgcn_s_setprio(0);
         dma_wait_barrier<ISSUES>();              // K[j+1] has landed
         if (j < ntiles) softmax(j);
@@ -428,12 +445,12 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
       b0 = bp1;
     }
   };
-  for (int i = tid; i < TILE / 16; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = tid; i < TILE_V / 16; i += kThreads) ((lds_u32x4_t*)vbuf(1))[i] = u32x4_t{0u, 0u, 0u, 0u};
   if (wave < kWaves / 2) {
 #pragma unroll
-    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, tile_off(0), 0u, kbuf(0), vbuf(0));
+    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, k_tile(0), 0u, kbuf(0), vbuf(0));
 #pragma unroll
-    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, tile_off(1), 0u, kbuf(1), vbuf(0));
+    for (int d = V_ISSUES; d < ISSUES; ++d) dma(d, k_tile(1), 0u, kbuf(1), vbuf(0));
   }
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -458,31 +475,32 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
       *(__attribute__((address_space(3))) u32x2_t*)(ost + lq * OS + db * 32 + 8 * jj + 4 * g) = w;
     }
   {
-    constexpr int CPR = D / 8;
+    constexpr int CPR = DV / 8;
     constexpr int RPI = 64 / CPR;
     const int cc = lane % CPR;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave / RPI; ++i) {
       const int r = i * RPI + lane / CPR;
       const u32x4_t w = *(const lds_u32x4_t*)(ost + r * OS + cc * 8);
-      if (qw0 + r < L) *(u32x4_t*)(p.o + (int64_t)(seq0 + qw0 + r) * H * D + (int64_t)h * D + cc * 8) = w;
+      if (qw0 + r < L) *(u32x4_t*)(p.o + (int64_t)(seq0 + qw0 + r) * H * DV + (int64_t)h * DV + cc * 8) = w;
     }
   }
   if (qrow < L && g == 0)
     p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
 }
 
-template <int D>
+template <int DQK, int DV>
 static hipError_t launch_fp8_dims(const Fp8Params& p, bool causal, hipStream_t s) {
   const dim3 grid(p.H * p.B * p.n_qblocks), block(kThreads);
-  if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, block, 0, s, p);
+  if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, DV, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, DV, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool causal, hipStream_t s) {
-  if (d == 64) return launch_fp8_dims<64>(p, causal, s);
-  if (d == 128) return launch_fp8_dims<128>(p, causal, s);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return launch_fp8_dims<64, 64>(p, causal, s);
+  if (d_qk == 128 && d_v == 128) return launch_fp8_dims<128, 128>(p, causal, s);
+  if (d_qk == 192 && d_v == 128) return launch_fp8_dims<192, 128>(p, causal, s);
   return hipErrorInvalidValue;
 }
 

@@ -32,10 +32,10 @@ struct FwdParams {
 // FP8 forward: q, k, v hold OCP E4M3 bytes; S = scale * q_descale * k_descale * Q K^T
 // and O = v_descale * P V / l.
 struct Fp8Params {
-  const uint8_t* q;           // e4m3 [T, H, d]
-  const uint8_t* k;           // e4m3 [T, H, d]
-  const uint8_t* v;           // e4m3 [T, H, d]
-  uint16_t* o;                // bf16 [T, H, d]
+  const uint8_t* q;           // e4m3 [T, H, d_qk]
+  const uint8_t* k;           // e4m3 [T, H, d_qk]
+  const uint8_t* v;           // e4m3 [T, H, d_v]
+  uint16_t* o;                // bf16 [T, H, d_v]
   float* lse;                 // fp32 [H, T]
   const int32_t* cu_seqlens;  // device int32 [B+1], or nullptr for fixed length N
   int B, H, N;
@@ -51,7 +51,7 @@ int query_block_rows();
 int keys_per_tile(int d_qk);
 int rows_per_wave();
 hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, int npoly, hipStream_t s);
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_exp2_debug(const float* x, float* y, int n, int use_poly, hipStream_t s);
 
 }  // namespace attn

@@ -188,10 +188,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * v rows with weights off by at most 2^-4 relative (2^-10 absolute below the
  * E4M3 normal range) each, and LSE carries the same weight error.
  *
- * q8, k8, v8: OCP E4M3 bytes [T, H, d] (token-major, heads interleaved);
- * o: bf16 [T, H, d]; lse: fp32 [H, T] (natural log of the scaled logits
- * scale * q . k).  cu_seqlens, B, H, N, causal: as attn_fwd.  Supported
- * d_qk = d_v = 64 or 128 (else ATTN_ERR_UNSUPPORTED).  scale: any finite
+ * q8, k8: OCP E4M3 bytes [T, H, d_qk], v8: [T, H, d_v] (token-major, heads
+ * interleaved); o: bf16 [T, H, d_v]; lse: fp32 [H, T] (natural log of the
+ * scaled logits scale * q . k).  cu_seqlens, B, H, N, causal: as attn_fwd.
+ * Supported (d_qk, d_v): attn_fwd's (64, 64), (128, 128), (192, 128) (else
+ * ATTN_ERR_UNSUPPORTED).  scale: any finite
  * value; q_descale, k_descale, v_descale: finite and > 0 (else
  * ATTN_ERR_VALUE).  Alignment: 16 bytes for q8, k8, v8, o; 4 for lse and
  * cu_seqlens.  Ownership, streams and errors as attn_fwd. */

@@ -152,16 +152,16 @@ def test_fp8_small_all_elements(d):
     check(f, o, lse, f"small d={d}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_ragged_packed_all_elements(causal, d):
+def test_fp8_ragged_packed_all_elements(causal, dims):
     lengths = [1, 63, 64, 65, 127, 128, 129, 300, 777]
-    inp = workloads.make_custom_inputs(lengths, H=3, d_qk=d, d_v=d, seed=11)
+    inp = workloads.make_custom_inputs(lengths, H=3, d_qk=dims[0], d_v=dims[1], seed=11)
     inp["causal"] = causal
     f = fp8_inputs(inp, prescale=(4.0, 2.0, 8.0))
-    say(f"case: fp8 ragged packed d={d} causal={causal} prescale (4, 2, 8)")
+    say(f"case: fp8 ragged packed dims={dims} causal={causal} prescale (4, 2, 8)")
     o, lse = run_fp8(f)
-    check(f, o, lse, f"ragged d={d} causal={causal}")
+    check(f, o, lse, f"ragged dims={dims} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -253,7 +253,7 @@ def test_fp8_agrees_with_bf16_kernel_on_the_same_values():
     assert np.all(np.abs(lse_f64(l8) - lse_f64(lb)) <= BL + 1e-3)
 
 
-@pytest.mark.parametrize("key", ["noncausal_b4h16n4096d128", "causal_b2h16n16384d128"])
+@pytest.mark.parametrize("key", ["noncausal_b4h16n4096d128", "causal_b2h16n16384d128", "causal_b2h32n8192dqk192dv128"])
 def test_fp8_full_size_sampled(key):
     inp = workloads.make_inputs(key)
     f = fp8_inputs(inp)
