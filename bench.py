@@ -317,7 +317,8 @@ def main():
     out = {
         "metric": ("attention bwd" if args.bwd else "attention fwd (FP8 E4M3 inputs)" if args.fp8
                    else "attention fwd" if bmask is None else "block-sparse attention fwd")
-                  + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X",
+                  + " TFLOP/s and % of BF16 MFMA peak on 1 MI355X"
+                  + (f", d={wl.d_qk}" if wl.d_qk == wl.d_v else f", d_qk={wl.d_qk} d_v={wl.d_v}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
