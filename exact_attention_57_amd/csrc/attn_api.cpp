@@ -87,6 +87,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   if ((int64_t)H * B * nqb > INT32_MAX) return ATTN_ERR_SHAPE;
   // token indices are 32-bit inside the kernel
   if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
+  // one sequence's K or V rows of one head are addressed through a 32-bit
+  // buffer range: N * H * d * 2 bytes must stay below 4 GiB
+  if ((int64_t)N * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
 
   attn::FwdParams p;
   p.q = static_cast<const uint16_t*>(q);

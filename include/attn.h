@@ -45,6 +45,8 @@
  * lse and cu_seqlens 4-byte aligned.
  *
  * Supported head dims (d_qk, d_v): (64, 64), (128, 128), (192, 128).
+ * N * H * max(d_qk, d_v) * 2 must be below 4 GiB (the K and V rows of one
+ * sequence are addressed through 32-bit buffer ranges); else ATTN_ERR_SHAPE.
  * Causal masking is square (query i sees keys j <= i of its own sequence).
  * scale: any finite value (negative values are handled exactly); when
  * |scale| * log2(e) < 1e-30 it is raised to 1e-30, which changes no output
