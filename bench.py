@@ -99,10 +99,16 @@ def compulsory_bytes(T, H, d_qk, d_v) -> float:
 
 
 def kernel_source_hash(family: str = "bf16") -> str:
+    """sha256[:16] of the kernel sources with comments and blank lines removed,
+    so that a change of wording leaves the traffic records valid."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[family]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,15 +10,16 @@ namespace attn {
 // FP8 (OCP E4M3) forward.
 //
 // The same work decode, ping-pong phases, LDS DMA pipeline and online softmax
-// as the bf16 kernel above, with both products on the gfx950 FP8 matrix
-// instruction v_mfma_f32_32x32x64_f8f6f4 (64-deep, twice the bf16 rate):
+// as the bf16 kernel (attn_fwd_kernel.hip), with both products on the gfx950
+// FP8 matrix instruction v_mfma_f32_32x32x64_f8f6f4 (64-deep, twice the bf16
+// rate), for (d_qk, d_v) = (64, 64), (128, 128) and (192, 128):
 //
-//   S^T = K Q^T      A: 32 bytes of one key row per lane (two ds_read_b128);
-//                    B: Q^T resident in 16 VGPRs
+//   S^T = K Q^T      A: 32 bytes of one key row per lane (two ds_read_b128)
+//                    per 64-deep step; B: Q^T resident (8 VGPRs per step)
 //   O^T += V^T P^T   A: V^T gathered by ds_read_b64_tr_b8 (four per operand);
 //                    B: the S^T accumulators after the softmax, rounded to E4M3
 //
-// plus a fifth output block whose A operand is all ones: each of its rows is
+// plus one more output block whose A operand is all ones: each of its rows is
 // the running row sum l of the E4M3-rounded P, so the softmax phase has no
 // row-sum additions and O / l is a weighted mean of V rows with the weights
 // the product actually used.  P <= 2^tau <= 256 stays inside E4M3's range
@@ -235,7 +236,7 @@ void attn_fwd_fp8_kernel(Fp8Params p) {
     }
   }
   auto prefetch_l2 = [&] __device__ (lds_u8_t* garbage) __attribute__((always_inline)) {
-    const int pw = wave - kWaves / 2;                  // 0..3 in group 1: one 128-byte row per lane
+    const int pw = wave - kWaves / 2;                  // 0..3 in group 1: one K or Q row per lane
     const uint32_t off = (uint32_t)(pw * 64 + lane) * k_rowbytes;
     dma_dword(pq_rsrc, off, (lds_u16_t*)garbage);
     dma_dword(pk_rsrc, off, (lds_u16_t*)garbage);

@@ -89,3 +89,16 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "single-GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for rel in sum(bench.KERNEL_SOURCES.values(), []):
+        dst = tmp_path / rel
+        os.makedirs(dst.parent, exist_ok=True)
+        dst.write_text("int f() {  // one\n  return 1; /* two */\n}\n")
+    h0 = bench.kernel_source_hash("bf16")
+    (tmp_path / bench.KERNEL_SOURCES["bf16"][0]).write_text("// new words\nint f() {  // other\n\n  return 1;\n}\n")
+    assert bench.kernel_source_hash("bf16") == h0
+    (tmp_path / bench.KERNEL_SOURCES["bf16"][0]).write_text("int f() {\n  return 2;\n}\n")
+    assert bench.kernel_source_hash("bf16") != h0
