@@ -72,10 +72,11 @@ def test_split_dims_two_tiles_per_block(causal):
     check(inp, causal, 1.0 / np.sqrt(192), mask, "packed ragged (192,128)", packed=True)
 
 
-def test_empty_query_blocks():
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+def test_empty_query_blocks(dims):
     """Whole query blocks with no kept key block, and a causal mask that hides
     the only kept block from some rows."""
-    inp = workloads.make_custom_inputs([600], 2, 128, 128, seed=23)
+    inp = workloads.make_custom_inputs([600], 2, dims[0], dims[1], seed=23)
     nb = 5
     mask = np.zeros((1, 2, nb, nb), dtype=np.uint8)
     mask[0, 0, 0, 0] = 1          # block row 0 keeps block 0

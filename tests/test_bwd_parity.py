@@ -92,9 +92,16 @@ def test_fixed_length_ragged_tail(causal):
     full_check(inp, causal, 1.0 / np.sqrt(128), "fixed N300 d128", packed=False)
 
 
-def test_empty_and_single_token_sequences():
-    inp = workloads.make_custom_inputs([0, 1, 0, 64, 5], 3, 64, 64, seed=7)
-    full_check(inp, True, 0.125, "empty and single-token sequences", packed=True)
+@pytest.mark.parametrize("dims", [(64, 64), (192, 128)])
+def test_empty_and_single_token_sequences(dims):
+    inp = workloads.make_custom_inputs([0, 1, 0, 64, 5], 3, dims[0], dims[1], seed=7)
+    full_check(inp, True, 1.0 / np.sqrt(dims[0]), f"empty and single-token sequences d{dims}", packed=True)
+
+
+def test_split_dims_negative_scale_and_large_logits():
+    inp = workloads.make_custom_inputs([200, 130], 2, 192, 128, seed=12, std=3.0)
+    full_check(inp, True, 0.25, "(192,128) std 3 inputs, scale 0.25", packed=True)
+    full_check(inp, False, -0.04, "(192,128) negative scale", packed=True)
 
 
 def test_large_logits_and_negative_scale():
