@@ -183,6 +183,17 @@ def test_fp8_empty_and_single_token_sequences():
         check(f, o, lse, f"empty+single causal={causal}", causal=causal)
 
 
+def test_fp8_non_power_of_two_descales():
+    """Descales that are not powers of two: the combined logit factor and the
+    output factor are rounded to fp32 in the library."""
+    inp = workloads.make_custom_inputs([300, 517], H=2, d_qk=128, d_v=128, seed=27)
+    inp["causal"] = True
+    f = fp8_inputs(inp, prescale=(3.7, 0.61, 11.3))
+    say("case: fp8 descales 1/3.7, 1/0.61, 1/11.3")
+    o, lse = run_fp8(f)
+    check(f, o, lse, "non-power-of-two descales")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_large_logits_exercise_rescaling(causal):
     """Peaked rows: std-3 inputs at scale 0.3 (logits of order +-100) make the
