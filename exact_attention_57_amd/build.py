@@ -29,7 +29,7 @@ LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
-DMA_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip"]   # kernels with inline-asm LDS DMAs
+DMA_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip"]   # kernels with LDS DMAs
 ARCH = "gfx950"
 
 

@@ -195,6 +195,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if ((int64_t)H * B * nb > INT32_MAX) return ATTN_ERR_SHAPE;   // one workgroup per (sequence, head, block)
   if ((int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;        // token indices are 32-bit in the kernels
   if ((int64_t)B * N * H > INT32_MAX) return ATTN_ERR_SHAPE;    // rows of the D pass
+  // one sequence's K or V rows of one head are addressed through a 32-bit buffer range
+  if ((int64_t)N * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
 
   attn_grad::BwdParams p;
   p.q = static_cast<const uint16_t*>(q);

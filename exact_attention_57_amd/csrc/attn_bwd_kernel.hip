@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include "attn_bwd_kernel.h"
+#include "attn_fwd_common.h"   // LDS DMA requests, buffer resources, barriers (namespace attn)
 
 namespace attn_grad {
 
@@ -118,16 +119,20 @@ __device__ __forceinline__ void seq_range(const BwdParams& p, int b, int& seq0, 
 // reverse: blocks of a pair in decreasing order (longest first for the
 // causal dQ kernel, whose block b visits b+1 key tiles).
 constexpr int kXcds = 8;
-__device__ __forceinline__ void decode_block(const BwdParams& p, bool reverse, int& h, int& b, int& blk) {
-  const int W = p.B * p.H * p.n_blocks;
+__device__ __forceinline__ void decode_block_n(const BwdParams& p, int n_blocks, bool reverse, int& h, int& b,
+                                               int& blk) {
+  const int W = p.B * p.H * n_blocks;
   const int i = blockIdx.x;
   const int x = i % kXcds, slot = i / kXcds;
   const int g = x * (W / kXcds) + min(x, W % kXcds) + slot;
-  const int pair = g / p.n_blocks;
-  blk = g - pair * p.n_blocks;
-  if (reverse) blk = p.n_blocks - 1 - blk;
+  const int pair = g / n_blocks;
+  blk = g - pair * n_blocks;
+  if (reverse) blk = n_blocks - 1 - blk;
   h = pair / p.B;
   b = pair - h * p.B;
+}
+__device__ __forceinline__ void decode_block(const BwdParams& p, bool reverse, int& h, int& b, int& blk) {
+  decode_block_n(p, p.n_blocks, reverse, h, b, blk);
 }
 
 template <bool V>
@@ -382,6 +387,154 @@ void bwd_dq_kernel(BwdParams p) {
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
 
+// ---- dQ with LDS DMA tiles (d_qk = d_v <= 128): one workgroup of 8 waves
+// (two per SIMD) per block of 256 query rows, so each K/V tile fetched from
+// L2 serves twice the rows of the 4-wave kernel above.  The tiles (K in the
+// row and the transposed layout, V in the row layout) are copied HBM/L2 ->
+// LDS by buffer_load ... lds, double-buffered: at the start of tile t every
+// wave issues its share of tile t+1's requests into the other buffer (last
+// read in tile t-1, before the barrier that ended it), computes tile t, then
+// waits for its requests and meets the others at the barrier, after which
+// tile t+1 is complete.  Rows past the sequence end read as zeros (the buffer
+// range ends after key L-1).  Per-wave arithmetic as in bwd_dq_kernel.
+#ifndef ATTN_BWD_DQ_DMA
+#define ATTN_BWD_DQ_DMA 1   // 0: the 4-wave register-staged dQ kernel at every head dim
+#endif
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = kDqWaves * kWave;
+constexpr int kDqBlock = kDqWaves * kRows;           // query rows per workgroup
+
+int dq_dma_block_rows() { return kDqBlock; }
+
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_dma_kernel(BwdParams p) {
+  static_assert(DQK == DV && DQK <= 128, "DMA dQ kernel: d_qk = d_v = 64 or 128");
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
+  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
+  constexpr int STAGE = 2 * K_ELEMS + V_ELEMS;        // K rows, K transposed, V rows
+  constexpr int OUT_ELEMS = kDqWaves * kRows * (DQK + 8);
+  constexpr int LDS_ELEMS = (2 * STAGE > OUT_ELEMS) ? 2 * STAGE : OUT_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
+  constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512;   // 1 KB requests per copy
+  constexpr int REQ = 2 * K_REQ + V_REQ;
+  static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0 && REQ % kDqWaves == 0, "request split");
+  constexpr int REQ_W = REQ / kDqWaves;                // requests per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  const int nblk = (p.N + kDqBlock - 1) / kDqBlock;
+  int h, b, blk;
+  decode_block_n(p, nblk, CAUSAL, h, b, blk);
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int q0 = blk * kDqBlock;
+  if (q0 >= L) return;                                 // uniform over the workgroup
+  const int qw0 = q0 + wave * kRows;
+  const int qrow = qw0 + lq;
+  const bool row_valid = qrow < L;
+
+  bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
+  load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
+  load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
+  const int T = total_tokens(p);
+  const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
+  const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
+  const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
+
+  const Reads<DQK> rk(lane);
+  const Reads<DV> rv(lane);
+  const int kend = CAUSAL ? min(L, q0 + kDqBlock) : L;
+  const int ntiles = (kend + kTile - 1) / kTile;
+  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
+  const uint32_t k_rowbytes = (uint32_t)(qk_stride * 2), v_rowbytes = (uint32_t)(v_stride * 2);
+  const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK,
+                                               (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
+  const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV,
+                                               (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
+  auto stage = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * STAGE; };
+
+  // this wave's requests for tile t into stage buffer st: request r of the
+  // tile (r = wave * REQ_W + i) fills 1 KB block rr of its copy; lane i writes
+  // the 16 bytes at LDS position 8 i of that block, i.e. chunk `pos` of row
+  // `row`, which holds the tile's chunk pos ^ f(row) of that row
+  auto issue = [&] __device__ (int t, int st) __attribute__((always_inline)) {
+    lds_u16_t* const base = stage(st);
+#pragma unroll
+    for (int i = 0; i < REQ_W; ++i) {
+      const int r = wave * REQ_W + i;                  // uniform
+      const int copy = r < K_REQ ? 0 : (r < 2 * K_REQ ? 1 : 2);
+      const int rr = r - copy * K_REQ;
+      const int D = copy < 2 ? DQK : DV;
+      const int e = rr * 512 + 8 * lane;               // element of the tile (row-major, D per row)
+      const int row = e / D, pos = (e % D) / 8;
+      const int f = copy == 0 ? RowSwz<DQK>::f(row) : (copy == 1 ? TrSwz<DQK>::f(row) : RowSwz<DV>::f(row));
+      const uint32_t rowbytes = copy < 2 ? k_rowbytes : v_rowbytes;
+      const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
+      const uint32_t tile_off = (uint32_t)(t * kTile) * rowbytes;
+      attn::dma_chunk(copy < 2 ? k_rsrc : v_rsrc, lane_off, tile_off,
+                      base + (copy == 0 ? 0 : (copy == 1 ? K_ELEMS : 2 * K_ELEMS)) + rr * 512);
+    }
+  };
+
+  f32x16_t dqacc[QBLK];
+#pragma unroll
+  for (int i = 0; i < QBLK; ++i) dqacc[i] = f32x16_t{};
+  const f32x16_t zero = {};
+
+  issue(0, 0);
+  attn::dma_wait_barrier<0>();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    const lds_u16_t* const k_row = stage(t & 1);
+    const lds_u16_t* const k_tr = k_row + K_ELEMS;
+    const lds_u16_t* const v_row = k_row + 2 * K_ELEMS;
+    const int k0 = t * kTile;
+    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(k_row, rk, ks, kb);
+      f32x16_t s = zero, dp = zero;
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], qreg[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
+#pragma unroll
+      for (int vs = 0; vs < V_STEPS; ++vs)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
+      float ds[16];
+      {
+        const int lim = masked ? key_lim - (k0 + kb * 32 + 8 * g) : 64;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
+          ds[r] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t dsb[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dsb[jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
+        bf16x8_t a_q[QBLK];
+#pragma unroll
+        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
+#pragma unroll
+        for (int db = 0; db < QBLK; ++db)
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
+      }
+    }
+    attn::dma_wait_barrier<0>();                       // tile t+1 has landed; stage t & 1 is free
+  }
+  store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
+}
+
 // ---- dK, dV with the work split over two wave groups: one workgroup of 8
 // waves per block of 128 key rows.  Waves 0-3 (dV group) own 32 keys each and
 // compute S = Q K^T, P and dV^T += dO^T P; waves 4-7 (dK group) own the same
@@ -629,12 +782,15 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   constexpr int RPB = kThreads / (DV / 8);
   hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, s, p);
   const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
-  if (causal) {
-    hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+  if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
+  else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
+  if constexpr (ATTN_BWD_DQ_DMA && DQK == DV && DQK <= 128) {
+    const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
+    if (causal) hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+    if (causal) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
 }

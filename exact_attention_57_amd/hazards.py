@@ -72,8 +72,11 @@ def check_function(name: str, instrs: list) -> list:
     return problems
 
 
-def scan(asm_text: str, kernel_substr: str = "attn_fwd_kernel"):
-    """Return (number of kernel functions with LDS DMAs, list of violations)."""
+def scan(asm_text: str, kernel_substr: str = ""):
+    """Return (number of kernel functions with LDS DMAs, list of violations).
+
+    Every function whose name contains ``kernel_substr`` (default: every
+    function) and that issues an LDS DMA is checked."""
     n, problems = 0, []
     for fn in re.split(r"\n(?=_Z\w+:)", asm_text):
         head = fn.split(":", 1)[0]

@@ -169,7 +169,8 @@ int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile,
  * contents on entry are ignored.  dq, dk, dv are overwritten.  cu_seqlens,
  * B, H, N, scale and causal must be the values of the forward call.
  * Supported (d_qk, d_v): (64, 64), (128, 128), (192, 128) (the forward's
- * pairs; others return ATTN_ERR_UNSUPPORTED).  Alignment: 16 bytes for the bf16 tensors, 4 for
+ * pairs; others return ATTN_ERR_UNSUPPORTED), with the forward's 4 GiB limit on
+ * one sequence's K or V rows of one head.  Alignment: 16 bytes for the bf16 tensors, 4 for
  * lse, delta and cu_seqlens.  Ownership, streams and errors as attn_fwd
  * (validation before any HIP call, asynchronous on `stream`). */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -139,6 +139,7 @@ def call_bwd(**kw):
     (dict(H=0), ea.ATTN_ERR_SHAPE),
     (dict(N=-1), ea.ATTN_ERR_SHAPE),
     (dict(B=2, N=2 ** 30 + 1), ea.ATTN_ERR_SHAPE),
+    (dict(H=64, N=262144), ea.ATTN_ERR_SHAPE),            # 4 GiB of K rows in one sequence
     (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=128, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),

@@ -54,7 +54,8 @@ def test_checker_flags_short_gaps():
 def test_safe_setting_has_no_hazards():
     build = _load("_attn_build_t", os.path.join(PKG, "build.py"))
     n, problems = hz.scan(build.kernel_asm(4))
-    assert n >= 24, f"expected every kernel instance to contain LDS DMAs, found {n}"
+    # 24 dense + 6 block-sparse bf16 forward, 6 FP8 forward, 4 backward dQ instances
+    assert n >= 40, f"expected every DMA kernel instance, found {n}"
     assert not problems, "\n".join(problems[:20])
 
 
@@ -64,4 +65,4 @@ def test_build_choice_is_hazard_free():
     nop = build.choose_dma_nop()
     assert nop in (0, 4)
     n, problems = hz.scan(build.kernel_asm(nop))
-    assert n >= 24 and not problems
+    assert n >= 40 and not problems
