@@ -1,4 +1,5 @@
-// Device-side pieces shared by the bf16 and FP8 forward kernels: wave and
+// Device-side pieces shared by the bf16 and FP8 forward kernels (and the
+// backward dQ kernel's LDS DMAs): wave and
 // workgroup geometry, cross-lane reductions, the LDS DMA requests with their
 // wait-state padding, buffer resources and the phase barriers.
 #ifndef EXACT_ATTENTION_57_AMD_ATTN_FWD_COMMON_H
