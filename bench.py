@@ -316,6 +316,19 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # per-launch spread, in a separate pass after the timed region (the events
+    # between launches would otherwise sit inside it)
+    n_each = min(args.steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_each)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    each = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    launch_ms = {"median": round(each[len(each) // 2], 4), "min": round(each[0], 4),
+                 "max": round(each[-1], 4), "launches": n_each}
+
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
     variant = "bwd" if args.bwd else "fp8" if args.fp8 else f"tau={args.tau},poly={args.poly},schedule={args.schedule}"
@@ -344,7 +357,7 @@ def main():
                    "packed": wl.varlen, "variant": variant, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel_ms": round(ev_ms, 4),
+                     "traffic": traffic, "kernel_ms": round(ev_ms, 4), "launch_ms": launch_ms,
                      "compulsory_bytes": compulsory_bytes(T, H, wl.d_qk, wl.d_v)},
     }
     if args.fp8:

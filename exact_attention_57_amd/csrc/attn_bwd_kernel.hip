@@ -600,20 +600,23 @@ void bwd_dkdv_split_kernel(BwdParams p) {
 
   TileRegs<DQK, kThreads2> qr;
   TileRegs<DV, kThreads2> dr;
-  float rowval = 0.0f;                      // threads 0..63: LSE (log2 units); 64..127: D
+  // threads 0..63: LSE, 64..127: D.  The LSE goes to log2 units only when it
+  // is staged: an arithmetic use right after the load would make the wave wait
+  // for every load in flight, the next tile's included.
+  float rowval = 0.0f;
   auto load_tile = [&] __device__ (int t) __attribute__((always_inline)) {
     const int q0t = qstart + t * kTile;
     tile_load<DQK, kThreads2>(qr, qbase, qk_stride, q0t, L, tid);
     tile_load<DV, kThreads2>(dr, dobase, v_stride, q0t, L, tid);
     const int r = q0t + (tid % kTile);
-    if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] * kLog2e : d_h[r]) : 0.0f;
+    if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] : d_h[r]) : 0.0f;
   };
   auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
   auto stage_tile = [&] __device__ (int t) __attribute__((always_inline)) {
     lds_u16_t* const base = buf(t);
     tile_store<DQK, true, !Q_ONCE, kThreads2>(qr, base, base + Q_ELEMS, tid);
     tile_store<DV, true, true, kThreads2>(dr, base + QS, base + QS + O_ELEMS, tid);
-    if (tid < 2 * kTile) ((lds_f32_t*)(base + QS + 2 * O_ELEMS))[tid] = rowval;
+    if (tid < 2 * kTile) ((lds_f32_t*)(base + QS + 2 * O_ELEMS))[tid] = tid < kTile ? rowval * kLog2e : rowval;
   };
   // this lane's 32 bytes of the P block of key slice wv, buffer i
   auto pslot = [&] __device__ (int i) __attribute__((always_inline)) {
