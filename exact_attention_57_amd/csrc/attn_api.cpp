@@ -88,8 +88,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   // token indices are 32-bit inside the kernel
   if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
   // one sequence's K or V rows of one head are addressed through a 32-bit
-  // buffer range: N * H * d * 2 bytes must stay below 4 GiB
-  if ((int64_t)N * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  // buffer range, and tile requests reach up to 255 rows past its end:
+  // (N + 256) * H * d * 2 bytes must stay below 4 GiB
+  if (((int64_t)N + 256) * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
 
   attn::FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -195,8 +196,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if ((int64_t)H * B * nb > INT32_MAX) return ATTN_ERR_SHAPE;   // one workgroup per (sequence, head, block)
   if ((int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;        // token indices are 32-bit in the kernels
   if ((int64_t)B * N * H > INT32_MAX) return ATTN_ERR_SHAPE;    // rows of the D pass
-  // one sequence's K or V rows of one head are addressed through a 32-bit buffer range
-  if ((int64_t)N * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  // one sequence's Q, K, V or dO rows of one head are addressed through a
+  // 32-bit buffer range, with tile requests up to 255 rows past its end
+  if (((int64_t)N + 256) * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
 
   attn_grad::BwdParams p;
   p.q = static_cast<const uint16_t*>(q);

@@ -45,8 +45,9 @@
  * lse and cu_seqlens 4-byte aligned.
  *
  * Supported head dims (d_qk, d_v): (64, 64), (128, 128), (192, 128).
- * N * H * max(d_qk, d_v) * 2 must be below 4 GiB (the K and V rows of one
- * sequence are addressed through 32-bit buffer ranges); else ATTN_ERR_SHAPE.
+ * (N + 256) * H * max(d_qk, d_v) * 2 must be below 4 GiB (the K and V rows of
+ * one sequence are addressed through 32-bit buffer ranges, and tile requests
+ * reach up to 255 rows past their end); else ATTN_ERR_SHAPE.
  * Causal masking is square (query i sees keys j <= i of its own sequence).
  * scale: any finite value (negative values are handled exactly); when
  * |scale| * log2(e) < 1e-30 it is raised to 1e-30, which changes no output
@@ -170,7 +171,7 @@ int attn_fwd_geometry(int d_qk, int d_v, int* rows_per_item, int* keys_per_tile,
  * B, H, N, scale and causal must be the values of the forward call.
  * Supported (d_qk, d_v): (64, 64), (128, 128), (192, 128) (the forward's
  * pairs; others return ATTN_ERR_UNSUPPORTED), with the forward's 4 GiB limit on
- * one sequence's K or V rows of one head.  Alignment: 16 bytes for the bf16 tensors, 4 for
+ * one sequence's rows of one head ((N + 256) * H * max(d_qk, d_v) * 2 bytes).  Alignment: 16 bytes for the bf16 tensors, 4 for
  * lse, delta and cu_seqlens.  Ownership, streams and errors as attn_fwd
  * (validation before any HIP call, asynchronous on `stream`). */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -73,6 +73,7 @@ def call(**kw):
     (dict(B=70000), ea.ATTN_ERR_SHAPE),
     (dict(N=65535 * ea.geometry(128, 128)["rows_per_item"] + 1), ea.ATTN_ERR_SHAPE),
     (dict(H=64, N=262144), ea.ATTN_ERR_SHAPE),            # 4 GiB of K rows in one sequence
+    (dict(H=64, N=262000), ea.ATTN_ERR_SHAPE),            # tile requests up to 255 rows past the end
     (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=128, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
@@ -140,6 +141,7 @@ def call_bwd(**kw):
     (dict(N=-1), ea.ATTN_ERR_SHAPE),
     (dict(B=2, N=2 ** 30 + 1), ea.ATTN_ERR_SHAPE),
     (dict(H=64, N=262144), ea.ATTN_ERR_SHAPE),            # 4 GiB of K rows in one sequence
+    (dict(H=64, N=262000), ea.ATTN_ERR_SHAPE),            # tile requests up to 255 rows past the end
     (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=128, d_v=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
