@@ -44,6 +44,10 @@
 #include "attn_bwd_kernel.h"
 #include "attn_fwd_common.h"   // LDS DMA requests, buffer resources, barriers (namespace attn)
 
+#ifndef ATTN_BWD_PREFETCH
+#define ATTN_BWD_PREFETCH 1  // dK/dV at d <= 128: a block's transposed operands read a phase early
+#endif
+
 namespace attn_grad {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -641,6 +645,24 @@ void bwd_dkdv_split_kernel(BwdParams p) {
     // carried from a block's first half to its second, in the same registers:
     // the dK group's dP (16 floats) or the dV group's P (8 dwords of bf16 pairs)
     f32x16_t carry = zero;
+    // The transposed A operands of the next block's dV (dO^T) or dK (Q^T)
+    // products, read at the end of half_a: that block's rows are visible from
+    // the barrier before half_a on (half_a reads them too), and a half_b that
+    // starts with its operands in registers does not wait for LDS first.
+    constexpr bool PRE = !Q_ONCE && ATTN_BWD_PREFETCH;
+    bf16x8_t pre[PRE ? 2 : 1][PRE ? ABLK : 1];
+    auto prefetch = [&] __device__ (int nb) __attribute__((always_inline)) {
+      if constexpr (PRE) {
+        const int t = nb / QB, qb = nb % QB;
+        const lds_u16_t* const base = buf(t);
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+  #pragma unroll
+          for (int db = 0; db < ABLK; ++db)
+            pre[hh][db] = KG ? read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh)
+                             : read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+      }
+    };
     // first half of block nb: dV group S, P -> LDS; dK group dP
     auto half_a = [&] __device__ (int nb) __attribute__((always_inline)) {
       const int t = nb / QB, qb = nb % QB;
@@ -692,6 +714,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
         for (int vs = 0; vs < V_STEPS; ++vs)
           carry = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], breg[vs], carry, 0, 0, 0);
       }
+      prefetch(nb);
     };
     // second half of block nb: dV group dV; dK group P from LDS, dS, dK
     auto half_b = [&] __device__ (int nb) __attribute__((always_inline)) {
@@ -705,7 +728,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
           const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw);
           bf16x8_t a_v[VBLK];
   #pragma unroll
-          for (int db = 0; db < VBLK; ++db) a_v[db] = read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+          for (int db = 0; db < VBLK; ++db)
+            a_v[db] = PRE ? pre[PRE ? hh : 0][PRE ? db : 0] : read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
   #pragma unroll
           for (int db = 0; db < VBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[db], bop, acc[db], 0, 0, 0);
         }
@@ -726,7 +750,9 @@ void bwd_dkdv_split_kernel(BwdParams p) {
           const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
           bf16x8_t a_k[KBLK];
   #pragma unroll
-          for (int db = 0; db < KBLK; ++db) a_k[db] = read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh);
+          for (int db = 0; db < KBLK; ++db)
+            a_k[db] = PRE ? pre[PRE ? hh : 0][PRE ? db : 0]
+                          : read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh);
   #pragma unroll
           for (int db = 0; db < KBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[db], bop, acc[db], 0, 0, 0);
         }
