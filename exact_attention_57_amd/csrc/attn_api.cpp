@@ -148,8 +148,9 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
   const int64_t nqb = ((int64_t)N + rows - 1) / rows;
   if ((int64_t)H * B * nqb > INT32_MAX) return ATTN_ERR_SHAPE;
   if (!cu_seqlens && (int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;
-  // a (sequence, head) K or V range is addressed by a 32-bit buffer resource
-  if ((int64_t)N * H * d_qk > INT32_MAX) return ATTN_ERR_SHAPE;
+  // a (sequence, head) K or V range is addressed by a 32-bit buffer resource,
+  // with tile requests up to 255 rows past its end
+  if (((int64_t)N + 256) * H * d_qk > INT32_MAX) return ATTN_ERR_SHAPE;
 
   attn::Fp8Params p;
   p.q = static_cast<const uint8_t*>(q8);

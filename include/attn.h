@@ -196,7 +196,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * interleaved); o: bf16 [T, H, d_v]; lse: fp32 [H, T] (natural log of the
  * scaled logits scale * q . k).  cu_seqlens, B, H, N, causal: as attn_fwd.
  * Supported (d_qk, d_v): attn_fwd's (64, 64), (128, 128), (192, 128) (else
- * ATTN_ERR_UNSUPPORTED).  scale: any finite
+ * ATTN_ERR_UNSUPPORTED); (N + 256) * H * d_qk must stay below 2^31 (bytes of
+ * one sequence's rows of one head, addressed through 32-bit buffer ranges;
+ * else ATTN_ERR_SHAPE).  scale: any finite
  * value; q_descale, k_descale, v_descale: finite and > 0 (else
  * ATTN_ERR_VALUE).  Alignment: 16 bytes for q8, k8, v8, o; 4 for lse and
  * cu_seqlens.  Ownership, streams and errors as attn_fwd. */

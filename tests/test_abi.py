@@ -190,6 +190,7 @@ def call_fp8(**kw):
     (dict(H=0), ea.ATTN_ERR_SHAPE),
     (dict(N=-1), ea.ATTN_ERR_SHAPE),
     (dict(H=64, N=2 ** 18 + 1), ea.ATTN_ERR_SHAPE),
+    (dict(H=64, N=262000), ea.ATTN_ERR_SHAPE),            # tile requests up to 255 rows past the end
     (dict(d_qk=64, d_v=128), ea.ATTN_ERR_UNSUPPORTED),
     (dict(d_qk=192, d_v=192), ea.ATTN_ERR_UNSUPPORTED),
     (dict(scale=math.nan), ea.ATTN_ERR_VALUE),
