@@ -21,10 +21,8 @@ __all__ = [
     "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "FP8_SUPPORTED_DIMS", "LIB_PATH",
 ]
 
-# EXACT_ATTENTION_57_AMD_LIB may point at another build of the same library
-# (e.g. a variant compiled with different tile settings) for comparisons.
-LIB_PATH = os.environ.get("EXACT_ATTENTION_57_AMD_LIB") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# The library built in-tree next to this file; no other copy is ever loaded.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_OK = 0
 ATTN_ERR_NULL = -1
@@ -124,6 +122,38 @@ def geometry(d_qk: int, d_v: int) -> dict:
     return {"rows_per_item": a.value, "keys_per_tile": b.value, "rows_per_wave": c.value}
 
 
+def _check_tensor(name, t, dtypes, device, shape=None, min_numel=None):
+    """Raise ValueError unless ``t`` is a contiguous tensor of one of ``dtypes`` on
+    ``device`` with exactly ``shape`` (or at least ``min_numel`` elements): the
+    kernels read and write these buffers at the sizes the C ABI states, so a
+    smaller or strided buffer would be accessed past its end."""
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _check_inputs(names_tensors, dtypes, what):
+    """Inputs of ``what``: contiguous GPU tensors of ``dtypes``, all on the first one's device."""
+    first = names_tensors[0][1]
+    if not first.is_cuda:
+        raise ValueError(f"{what}: {names_tensors[0][0]} must be a CUDA tensor")
+    for name, t in names_tensors:
+        _check_tensor(name, t, dtypes, first.device)
+    return first.device
+
+
+def _check_stats(stats, device):
+    import torch
+    _check_tensor("stats", stats, (torch.int64, torch.uint64), device, min_numel=4)
+
+
 def default_opts() -> FwdOpts:
     o = FwdOpts()
     lib.attn_fwd_opts_default(ctypes.byref(o))
@@ -187,29 +217,31 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
     allocated with torch when not given.  ``stats``: optional uint64/int64
     device tensor of 4 counters that the kernel adds to.  ``block_mask``:
     optional uint8/bool device tensor [B, H, nb, nb], nb = ceil(N / 128), for
-    block-sparse attention (see attn_fwd_opts in include/attn.h).
+    block-sparse attention (see attn_fwd_opts in include/attn.h).  Every
+    buffer given is checked for dtype, shape (o like v, lse [H, T]),
+    contiguity and device before the call; ValueError otherwise.
     """
     import torch
     B, N, H, T, d_qk = _fwd_shape(q, cu_seqlens, max_seqlen)
     d_v = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    dev = _check_inputs((("q", q), ("k", k), ("v", v)), (torch.bfloat16,), "fwd")
     if k.shape != q.shape or v.shape[:-1] != q.shape[:-1]:
         raise ValueError("q, k, v shapes disagree")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev, shape=(B + 1,))
     if o is None:
         o = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+    _check_tensor("o", o, (torch.bfloat16,), dev, shape=v.shape)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_tensor("lse", lse, (torch.float32,), dev, shape=(H, T))
+    if stats is not None:
+        _check_stats(stats, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d_qk)
     if block_mask is not None:
         nb = (N + 127) // 128
-        if (block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous()
-                or not block_mask.is_cuda or tuple(block_mask.shape) != (B, H, nb, nb)):
-            raise ValueError(f"block_mask must be a contiguous uint8/bool CUDA tensor of shape {(B, H, nb, nb)}")
+        _check_tensor("block_mask", block_mask, (torch.uint8, torch.bool), dev, shape=(B, H, nb, nb))
     opts = FwdOpts(float(rescale_threshold_log2), int(poly_exp_sixteenths), int(schedule),
                    stats.data_ptr() if stats is not None else None,
                    block_mask.data_ptr() if block_mask is not None else None)
@@ -238,17 +270,17 @@ def fwd_fp8(q8, k8, v8, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, c
     import torch
     B, N, H, T, d_qk = _fwd_shape(q8, cu_seqlens, max_seqlen)
     d_v = v8.shape[-1]
-    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
-        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous float8_e4m3fn/uint8 CUDA tensor")
+    dev = _check_inputs((("q8", q8), ("k8", k8), ("v8", v8)), (torch.float8_e4m3fn, torch.uint8), "fwd_fp8")
     if k8.shape != q8.shape or v8.shape[:-1] != q8.shape[:-1]:
         raise ValueError("q8, k8, v8 shapes disagree")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev, shape=(B + 1,))
     if o is None:
         o = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device)
+    _check_tensor("o", o, (torch.bfloat16,), dev, shape=v8.shape)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q8.device)
+    _check_tensor("lse", lse, (torch.float32,), dev, shape=(H, T))
     if scale is None:
         scale = 1.0 / math.sqrt(d_qk)
     st = fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -274,8 +306,10 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False
     Shapes and layouts as ``fwd`` (o and dout shaped like v; lse [H, T] as
     ``fwd`` returned it); the same cu_seqlens / max_seqlen / causal / scale
     as the forward call.  Returns (dq, dk, dv), bf16, allocated with torch
-    when not given; ``delta`` (fp32, at least H*B*N elements) is the
-    workspace for the row terms D = rowsum(dout * o).
+    when not given; ``delta`` (contiguous fp32, at least H*T elements, T the
+    total token count) is the workspace for the row terms D = rowsum(dout * o).
+    Every buffer is checked for dtype, shape (dq, dk, dv like q, k, v; lse
+    [H, T]), contiguity and device before the call; ValueError otherwise.
     """
     import torch
     if q.dim() == 4:
@@ -297,22 +331,22 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False
     else:
         raise ValueError("q must be [B, N, H, d] or [T, H, d]")
     d_v = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    T = B * N if q.dim() == 4 else q.shape[0]
+    dev = _check_inputs((("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), (torch.bfloat16,), "bwd")
     if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or o.shape != v.shape or dout.shape != v.shape:
         raise ValueError("q, k, v, o, dout shapes disagree")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 CUDA tensor")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    _check_tensor("lse", lse, (torch.float32,), dev, shape=(H, T))
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev, shape=(B + 1,))
     dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device) if dv is None else dv
+    _check_tensor("dq", dq, (torch.bfloat16,), dev, shape=q.shape)
+    _check_tensor("dk", dk, (torch.bfloat16,), dev, shape=k.shape)
+    _check_tensor("dv", dv, (torch.bfloat16,), dev, shape=v.shape)
     if delta is None:
-        delta = torch.empty(H * B * N, dtype=torch.float32, device=q.device)
-    elif delta.dtype != torch.float32 or delta.numel() < H * B * N or not delta.is_cuda:
-        raise ValueError("delta must be an fp32 CUDA tensor of at least H*B*N elements")
+        delta = torch.empty(H * T, dtype=torch.float32, device=q.device)
+    _check_tensor("delta", delta, (torch.float32,), dev, min_numel=H * T)
     if scale is None:
         scale = 1.0 / math.sqrt(d_qk)
     st = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
@@ -327,10 +361,10 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False
 def debug_exp2(x, use_poly: bool, y=None, stream=None):
     """The kernels' own exp2 (hardware or software cubic) over a fp32 CUDA tensor."""
     import torch
-    if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
-        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    dev = _check_inputs((("x", x),), (torch.float32,), "debug_exp2")
     if y is None:
         y = torch.empty_like(x)
+    _check_tensor("y", y, (torch.float32,), dev, shape=x.shape)
     st = int(lib.attn_debug_exp2(x.data_ptr(), y.data_ptr(), x.numel(), int(bool(use_poly)),
                                  _stream_handle(stream)))
     if st != ATTN_OK:

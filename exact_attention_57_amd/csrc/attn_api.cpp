@@ -13,6 +13,11 @@ namespace {
 
 constexpr int kVersion = 400;  // 0.4.0
 constexpr int kMaxGridYZ = 65535;
+// Largest conditional-rescale threshold (log2 units).  A row that skips its
+// rescale weights keys by up to 2^tau, so its row sum and output accumulators
+// grow to about N * 2^tau * max|v| in fp32; 64 keeps that far below the fp32
+// range (2^128) for any sequence the 32-bit token indices allow.
+constexpr float kMaxRescaleThreshold = 64.0f;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -66,7 +71,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
   if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
-  if (!isfinite(op.rescale_threshold_log2)) return ATTN_ERR_VALUE;
+  if (!isfinite(op.rescale_threshold_log2) || op.rescale_threshold_log2 > kMaxRescaleThreshold) return ATTN_ERR_VALUE;
   const int np = op.poly_exp_sixteenths;
   if (np != 0 && np != 2 && np != 4 && np != 8) return ATTN_ERR_VALUE;
   if (op.schedule != ATTN_SCHEDULE_LONGEST_FIRST && op.schedule != ATTN_SCHEDULE_NATURAL) return ATTN_ERR_VALUE;

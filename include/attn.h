@@ -91,7 +91,10 @@ typedef struct attn_fwd_opts {
   /* Conditional-rescale threshold in log2 units.  >= 0: rescale a row only
    * when the tile's row max exceeds the kept max by more than this (0 gives
    * results bitwise equal to always rescaling).  < 0: always rescale, the
-   * classic online softmax.  Default 8.0 (a factor of 256). */
+   * classic online softmax.  Default 8.0 (a factor of 256).  At most 64
+   * (else ATTN_ERR_VALUE): a row that skips its rescale weights keys by up
+   * to 2^threshold, and its fp32 row sum and output accumulators must stay
+   * far below the fp32 range; non-finite values are rejected too. */
   float rescale_threshold_log2;
   /* Sixteenths of the exponentials computed with the software exp2:
    * one of 0, 2, 4, 8 (0, 1/8, 1/4, 1/2).  Default 0. */

@@ -95,11 +95,21 @@ def test_validation_codes(kw, code):
 @pytest.mark.parametrize("field,value", [
     ("poly_exp_sixteenths", 3), ("poly_exp_sixteenths", 16), ("poly_exp_sixteenths", -2),
     ("schedule", 2), ("rescale_threshold_log2", math.inf), ("rescale_threshold_log2", math.nan),
+    ("rescale_threshold_log2", 64.5), ("rescale_threshold_log2", 200.0),
 ])
 def test_option_validation(field, value):
     o = ea.default_opts()
     setattr(o, field, value)
     assert call(opts=o) == ea.ATTN_ERR_VALUE
+
+
+@pytest.mark.parametrize("tau,code", [(64.0, ea.ATTN_OK), (64.001, ea.ATTN_ERR_VALUE), (-5.0, ea.ATTN_OK)])
+def test_rescale_threshold_bound(tau, code):
+    """Thresholds up to 64 (log2 units) are accepted; larger ones are rejected
+    before anything runs (N = 0 returns after the option checks)."""
+    o = ea.default_opts()
+    o.rescale_threshold_log2 = tau
+    assert call(N=0, q=None, k=None, v=None, o=None, lse=None, opts=o) == code
 
 
 def test_misaligned_stats_rejected():

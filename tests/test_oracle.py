@@ -252,6 +252,70 @@ def test_online_softmax_threshold_zero_equals_unconditional_bitwise():
     assert c[2]["considered"] == a[2]["considered"]
 
 
+# Hand-built rescale counts.  scale = ln 2 makes c = scale * log2(e) exactly 1
+# in fp64, so integer logits are exact in log2 units.  Query row 0 and row 1
+# see ten keys in tiles of two; the tiles' maxima are
+#     row 0: 0, 9, 16, 17, 10     (rises over the kept max: 9, 7, 8.0, 1)
+#     row 1: 5, 5, 14, 20, 31     (rises: 0, 9, 6, 17)
+# With the strict rule "rescale iff tile max - kept max > tau": tau = 8 takes
+# row 0's first rise only (7 stays below and 8.0 is not above) and row 1's
+# rises of 9 and 17; tau = 7 also takes row 0's 8.0; tau = 0 takes every
+# strict increase; tau < 0 takes every tile after the first.
+_HB_LOGITS = ([0, -3, 9, 2, 16, 1, 17, 0, 10, 5], [5, -1, 5, 4, 14, 3, 20, -7, 31, 0])
+_HB_TAKEN = {8.0: (1, 2), 7.0: (2, 2), 0.0: (3, 3), -1.0: (4, 4)}
+
+
+def _hand_built_counts(model, tau):
+    """(taken, considered) of rows 0 and 1 (each repeated as 10 query rows), and the
+    O, LSE of one row of each, from an online-softmax model function."""
+    k = np.zeros((10, 1, 2))
+    k[:, 0, 0], k[:, 0, 1] = _HB_LOGITS
+    v = np.arange(20, dtype=np.float64).reshape(10, 1, 2)
+    out = []
+    for row in (0, 1):
+        q = np.zeros((10, 1, 2))
+        q[:, 0, row] = 1.0                                    # logits of every query row = column `row` of k
+        O, L, st = model(q, k, v, np.array([0, 10]), False, math.log(2.0), tau=tau, tile=2)
+        out.append((st["taken"] / 10, st["considered"] / 10, O[0, 0], L[0, 0]))
+    return out
+
+
+@pytest.mark.parametrize("tau", sorted(_HB_TAKEN))
+def test_online_softmax_rescale_counts_hand_built(tau):
+    assert math.log(2.0) * (1.0 / math.log(2.0)) == 1.0
+    v = np.arange(20, dtype=np.float64).reshape(10, 2)
+    for row, (taken, considered, O, L) in enumerate(_hand_built_counts(online_softmax_attention_f64, tau)):
+        assert considered == 4
+        assert taken == _HB_TAKEN[tau][row], (tau, row, taken)
+        # whatever was skipped, the result is the plain definition
+        w = np.array([2.0 ** x for x in _HB_LOGITS[row]])
+        assert abs(L - math.log(w.sum())) <= 1e-12
+        assert np.max(np.abs(O - (w / w.sum()) @ v)) <= 1e-10
+
+
+_MODEL_PLANTS = {
+    "non-strict rule": ("(m_t - m > tau)", "(m_t - m >= tau)"),
+    "first tile counted": ("taken += int(np.count_nonzero(do & ~fresh))", "taken += int(np.count_nonzero(do))"),
+    "max follows every tile": ("m_new = np.where(do, m_t, m)", "m_new = np.where(visible, np.maximum(m, m_t), m)"),
+}
+
+
+@pytest.mark.parametrize("plant", sorted(_MODEL_PLANTS))
+def test_rescale_count_pin_catches_planted_mistakes(plant):
+    """Each plausible mistake in the model's rescale rule, planted in a copy of
+    its source, changes a hand-built count."""
+    import inspect
+    import oracle.online_softmax as mod
+    old, new = _MODEL_PLANTS[plant]
+    src = inspect.getsource(mod)
+    assert src.count(old) == 1
+    ns = {}
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    wrong = ns["online_softmax_attention_f64"]
+    got = {tau: tuple(r[0] for r in _hand_built_counts(wrong, tau)) for tau in _HB_TAKEN}
+    assert got != _HB_TAKEN, f"planted '{plant}' went unnoticed"
+
+
 # ----------------------------------------------------------- planted mistakes
 
 class _NpProxy:
