@@ -2,8 +2,8 @@
 """Benchmark of the fused attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
-                    [--tau 8.0] [--poly 0] [--no-cpu-baseline] [--bwd]
-                    [--block-density D] [--fp8]
+                    [--tau 8.0] [--poly 0] [--schedule 0|1] [--no-cpu-baseline]
+                    [--bwd] [--block-density D] [--fp8] [--stamps] [--stats]
 
 A step is one call of attn_fwd over the whole workload (all query blocks of
 all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
@@ -40,6 +40,15 @@ an all-ones mask counts exactly the dense figure).
 --fp8 runs the FP8 forward pass (attn_fwd_fp8) on the same draws rounded to
 E4M3 (descales 1); same FLOP convention, roofline against the dense FP8
 MFMA peak (5.0 PFLOP/s), with the percentage of the bf16 peak alongside.
+
+--stamps times the instrumented build of the bf16 forward pass
+(libattn_stamps.so: the same kernels plus per-workgroup clock stamps), then
+runs it once more with a record buffer and adds a "stamps" summary: the
+XCD each workgroup ran on against its grid index, per-XCD and per-CU busy
+time, the finish-time tail (last workgroup end minus the median end), the
+start order against the grid index and against the work per item, and the
+shader cycles per tile iteration of each phase (matrix, barrier, softmax,
+barrier) for one wave of each ping-pong group.
 """
 from __future__ import annotations
 
@@ -181,6 +190,94 @@ def cpu_baseline(inp, budget_s: float = 10.0, backward_dout=None, block_mask=Non
             "seconds": round(dt, 3), "cpu": _cpu_model(), "blas": blas, "host_cpus": os.cpu_count()}
 
 
+STAMP_WORDS = 16              # uint64 per workgroup record of the instrumented build
+REALTIME_HZ = 100e6           # s_memrealtime rate
+
+
+def stamp_summary(ea, q, k, v, o, lse, cu, inp, wl, args, bmask_dev, stream, fwd_lib, kernel_ms) -> dict:
+    """One launch of the instrumented build with a record buffer, summarised.
+
+    Record words (per workgroup, at its linear grid index): [0] real-time clock
+    at entry, [1] at the end, [2] (XCC id << 32) | HW_ID, [3] work item, [4]
+    tile-loop iterations, [5..7] shader cycles of the prologue, the loop and
+    the epilogue (wave 0), [8..11] wave 0's loop cycles in its matrix phases,
+    the barrier after them, its softmax phases and the barrier after those,
+    [12..15] the same for wave 4."""
+    import numpy as np
+    import torch
+    geo = ea.geometry(wl.d_qk, wl.d_v)
+    nqb = -(-inp["N"] // geo["rows_per_item"])
+    W = inp["B"] * inp["H"] * nqb
+    buf = torch.zeros(4 + STAMP_WORDS * W, dtype=torch.int64, device="cuda")
+    ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal, scale=inp["scale"],
+           rescale_threshold_log2=args.tau, poly_exp_sixteenths=args.poly, schedule=args.schedule,
+           block_mask=bmask_dev, stats=buf, stream=stream, _lib=fwd_lib)
+    torch.cuda.synchronize()
+    r = buf[4:].cpu().numpy().view(np.uint64).reshape(W, STAMP_WORDS).astype(np.float64)
+    ran = r[:, 4] > 0                                        # workgroups with a query block to compute
+    t0 = r[:, 0].min()
+    start = (r[:, 0] - t0) / REALTIME_HZ * 1e6               # us
+    end = (r[:, 1] - t0) / REALTIME_HZ * 1e6
+    span = float(end.max())
+    hw = buf[4:].cpu().numpy().view(np.uint64).reshape(W, STAMP_WORDS)[:, 2]
+    xcc = (hw >> np.uint64(32)).astype(np.int64)
+    cu_key = xcc * 256 + ((hw >> np.uint64(8)) & np.uint64(0xff)).astype(np.int64)   # XCC, SE, SH, CU
+    ids = np.arange(W)
+    dur = end - start
+    per_cu = {}
+    for key, d in zip(cu_key[ran], dur[ran]):
+        per_cu[key] = per_cu.get(key, 0.0) + d
+    cu_busy = np.array(list(per_cu.values()))
+    xcds = {}
+    for x in range(8):
+        sel = ran & (xcc == x)
+        if sel.any():
+            xcds[str(x)] = {"workgroups": int(sel.sum()), "first_start_us": round(float(start[sel].min()), 2),
+                            "last_end_us": round(float(end[sel].max()), 2),
+                            "busy_us": round(float(dur[sel].sum()), 1)}
+    e_ran = np.sort(end[ran])
+    iters = r[ran, 4]
+    loop = r[ran, 6]
+    ph = r[ran, 8:16] / iters[:, None]                       # cycles per loop iteration
+    cyc = r[ran, 5] + r[ran, 6] + r[ran, 7]
+    clock_ghz = cyc / np.maximum((r[ran, 1] - r[ran, 0]) / REALTIME_HZ, 1e-12) / 1e9
+
+    def rank_corr(a, b):
+        ra, rb = np.argsort(np.argsort(a)), np.argsort(np.argsort(b))
+        return float(np.corrcoef(ra, rb)[0, 1]) if len(a) > 2 else None
+
+    # longest first: within each XCD, do workgroups with more tile iterations start earlier?
+    lf = [rank_corr(start[ran & (xcc == x)], r[ran & (xcc == x), 4]) for x in range(8)
+          if (ran & (xcc == x)).sum() > 2 and np.ptp(r[ran & (xcc == x), 4]) > 0]
+    names = ["matrix", "barrier_after_matrix", "softmax", "barrier_after_softmax"]
+    return {
+        "workgroups": int(W), "workgroups_with_work": int(ran.sum()),
+        "kernel_ms_instrumented": round(kernel_ms, 4),
+        "span_us": round(span, 1),
+        "xcc_equals_index_mod_8": round(float(np.mean(xcc == ids % 8)), 4),
+        "per_xcd": xcds,
+        "cus_used": int(len(per_cu)),
+        "cu_busy_us": {"max": round(float(cu_busy.max()), 1), "mean": round(float(cu_busy.mean()), 1),
+                       "min": round(float(cu_busy.min()), 1)},
+        "finish_us": {"median": round(float(np.median(e_ran)), 1), "last": round(float(e_ran[-1]), 1),
+                      "tail_last_minus_median": round(float(e_ran[-1] - np.median(e_ran)), 1),
+                      "p90": round(float(np.percentile(e_ran, 90)), 1)},
+        "start_order_vs_index_rank_corr": rank_corr(start[ran], ids[ran]),
+        "start_vs_tiles_rank_corr_per_xcd": [round(x, 3) for x in lf] if lf else None,
+        "workgroup_us": {"median": round(float(np.median(dur[ran])), 2), "max": round(float(dur[ran].max()), 2)},
+        "tile_iterations": {"median": float(np.median(iters)), "max": float(iters.max())},
+        "cycles_per_iteration": {
+            "wave0_group0": {n: round(float(np.mean(ph[:, i])), 1) for i, n in enumerate(names)},
+            "wave4_group1": {n: round(float(np.mean(ph[:, 4 + i])), 1) for i, n in enumerate(names)},
+            "loop_total": round(float(np.mean(loop / iters)), 1),
+        },
+        "cycles_per_workgroup": {"prologue": round(float(np.mean(r[ran, 5])), 0),
+                                 "loop": round(float(np.mean(loop)), 0),
+                                 "epilogue": round(float(np.mean(r[ran, 7])), 0)},
+        "shader_clock_ghz": {"median": round(float(np.median(clock_ghz)), 3)},
+    }
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -215,6 +312,10 @@ def main():
                     help="with --block-density: query-block rows 2i+1 copy rows 2i (the 256-row work items "
                          "then keep exactly the drawn fraction of key tiles)")
     ap.add_argument("--fp8", action="store_true", help="time the FP8 (E4M3) forward pass (attn_fwd_fp8)")
+    ap.add_argument("--stamps", action="store_true",
+                    help="time the instrumented build (libattn_stamps.so) of the bf16 forward pass and summarise "
+                         "its per-workgroup records: dispatch order, XCD mapping, per-CU balance, finish tail, "
+                         "cycles per phase")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
@@ -270,10 +371,17 @@ def main():
         bmask_dev = torch.from_numpy(bmask).cuda()
         flops = block_sparse_flops(lengths, H, wl.d_qk, wl.d_v, wl.causal, bmask)
 
+    fwd_lib = None
+    if args.stamps:
+        if args.bwd or args.fp8:
+            raise SystemExit("--stamps instruments the bf16 forward pass")
+        fwd_lib = ea.check_build("stamps")
+
     def step():
         ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
                scale=inp["scale"], rescale_threshold_log2=args.tau,
-               poly_exp_sixteenths=args.poly, schedule=args.schedule, block_mask=bmask_dev, stream=stream)
+               poly_exp_sixteenths=args.poly, schedule=args.schedule, block_mask=bmask_dev, stream=stream,
+               _lib=fwd_lib)
 
     f8 = None
     if args.fp8:
@@ -380,6 +488,10 @@ def main():
         out["stats"] = {"rescale_considered": considered, "rescale_taken": taken,
                         "skip_rate": round(1.0 - taken / considered, 4) if considered else None,
                         "wave_tiles": tiles, "work_items": items}
+    if args.stamps:
+        out["metric"] = "instrumented build: " + out["metric"]
+        out["stamps"] = stamp_summary(ea, q, k, v, o, lse, cu, inp, wl, args, bmask_dev, stream, fwd_lib,
+                                      ev_ms)
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, dout_bits if args.bwd else None, bmask, f8)

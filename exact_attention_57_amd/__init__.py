@@ -18,7 +18,7 @@ __all__ = [
     "AttnError", "lib", "fwd", "fwd_raw", "fwd_fp8", "fwd_fp8_raw", "bwd", "bwd_raw", "debug_exp2", "strerror", "version", "geometry",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
     "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
-    "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "FP8_SUPPORTED_DIMS", "LIB_PATH",
+    "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "FP8_SUPPORTED_DIMS", "LIB_PATH", "CHECK_BUILDS", "check_build",
 ]
 
 # The library built in-tree next to this file; no other copy is ever loaded.
@@ -67,15 +67,18 @@ def _hip_runtimes_mapped():
     return found
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+CHECK_BUILDS = ("racecheck", "stamps")
+
+
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python exact_attention_57_amd/build.py`")
+            f"{path} is missing: build it with `python exact_attention_57_amd/build.py`")
     # torch ships its own HIP runtime.  Load it first so that libattn.so's
     # dependency on libamdhip64.so.7 resolves to that same, already-loaded
     # copy: two HIP runtimes in one process cannot share streams or memory.
     import torch  # noqa: F401
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise ImportError(f"more than one HIP runtime is loaded: {sorted(runtimes)}")
@@ -103,6 +106,20 @@ def _load():
 
 
 lib = _load()
+_check_libs = {}
+
+
+def check_build(name: str):
+    """ctypes handle of one of the checking builds compiled next to libattn.so
+    from the same sources: ``"racecheck"`` (every barrier drains all memory
+    traffic and is passed twice) or ``"stamps"`` (the forward kernels write
+    per-workgroup timing records after the statistics counters).  Pass it as
+    ``_lib`` to ``fwd``, ``fwd_fp8`` or ``bwd``."""
+    if name not in CHECK_BUILDS:
+        raise ValueError(f"unknown checking build {name!r}; one of {CHECK_BUILDS}")
+    if name not in _check_libs:
+        _check_libs[name] = _load(os.path.join(os.path.dirname(LIB_PATH), f"libattn_{name}.so"))
+    return _check_libs[name]
 
 
 def strerror(status: int) -> str:
@@ -161,9 +178,9 @@ def default_opts() -> FwdOpts:
 
 
 def fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, B, H, N, d_qk, d_v, scale, causal,
-            stream, opts: FwdOpts | None = None) -> int:
+            stream, opts: FwdOpts | None = None, _lib=None) -> int:
     """Call attn_fwd_ex with raw integer pointers; returns the status code."""
-    return int(lib.attn_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
+    return int((_lib or lib).attn_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
                                int(d_qk), int(d_v), float(scale), int(bool(causal)), stream,
                                ctypes.byref(opts) if opts is not None else None))
 
@@ -205,7 +222,7 @@ def _fwd_shape(q, cu_seqlens, max_seqlen):
 
 def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
         scale=None, rescale_threshold_log2=8.0, poly_exp_sixteenths=0,
-        schedule=SCHEDULE_LONGEST_FIRST, stats=None, block_mask=None, stream=None):
+        schedule=SCHEDULE_LONGEST_FIRST, stats=None, block_mask=None, stream=None, _lib=None):
     """Fused attention forward on torch tensors.
 
     Fixed length: q, k [B, N, H, d_qk], v [B, N, H, d_v] (or [T, H, d] with
@@ -247,22 +264,22 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
                    block_mask.data_ptr() if block_mask is not None else None)
     st = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), opts)
+                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), opts, _lib=_lib)
     if st != ATTN_OK:
         raise AttnError(st)
     return o, lse
 
 
 def fwd_fp8_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, B, H, N, d_qk, d_v, scale,
-                q_descale, k_descale, v_descale, causal, stream) -> int:
+                q_descale, k_descale, v_descale, causal, stream, _lib=None) -> int:
     """Call attn_fwd_fp8 with raw integer pointers; returns the status code."""
-    return int(lib.attn_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
+    return int((_lib or lib).attn_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(N),
                                 int(d_qk), int(d_v), float(scale), float(q_descale), float(k_descale),
                                 float(v_descale), int(bool(causal)), stream))
 
 
 def fwd_fp8(q8, k8, v8, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=False,
-            scale=None, q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None):
+            scale=None, q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None, _lib=None):
     """FP8 attention forward: q8, k8, v8 hold OCP E4M3 values (torch.float8_e4m3fn
     or uint8 bit patterns), contiguous CUDA tensors shaped as for ``fwd``, each
     multiplied by its descale factor.  Returns (o bf16 shaped like v8, lse fp32
@@ -285,21 +302,22 @@ def fwd_fp8(q8, k8, v8, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, c
         scale = 1.0 / math.sqrt(d_qk)
     st = fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                     B, H, N, d_qk, d_v, scale, q_descale, k_descale, v_descale, causal, _stream_handle(stream))
+                     B, H, N, d_qk, d_v, scale, q_descale, k_descale, v_descale, causal, _stream_handle(stream),
+                     _lib=_lib)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
     return o, lse
 
 
 def bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr, cu_ptr,
-            B, H, N, d_qk, d_v, scale, causal, stream) -> int:
+            B, H, N, d_qk, d_v, scale, causal, stream, _lib=None) -> int:
     """Call attn_bwd with raw integer pointers; returns the status code."""
-    return int(lib.attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr, cu_ptr,
+    return int((_lib or lib).attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr, cu_ptr,
                             int(B), int(H), int(N), int(d_qk), int(d_v), float(scale), int(bool(causal)), stream))
 
 
 def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False, scale=None,
-        dq=None, dk=None, dv=None, delta=None, stream=None):
+        dq=None, dk=None, dv=None, delta=None, stream=None, _lib=None):
     """Attention backward on torch tensors: gradients of the forward's o with
     respect to q, k, v for the output gradient ``dout``.
 
@@ -352,7 +370,7 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False
     st = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                  cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream))
+                 B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), _lib=_lib)
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv

@@ -12,6 +12,17 @@ The build first compiles the kernels to assembly with one wait state
 (``ATTN_DMA_NOP=0``) and scans it (``hazards.py``); it keeps that setting only
 if no LDS DMA reads an SGPR a VALU instruction wrote fewer than five wait
 states earlier, and otherwise builds with five (``ATTN_DMA_NOP=4``).
+
+Two checking builds of the same sources are written next to the library,
+both with the always-safe five wait states:
+
+  libattn_racecheck.so  ATTN_RACE_CHECK=1: every barrier drains all memory
+                        traffic and is passed twice (outputs must equal the
+                        default build's bit for bit)
+  libattn_stamps.so     ATTN_STAMPS=1: the forward kernels write per-workgroup
+                        timing records after the statistics counters
+
+Object files are compiled in parallel.
 """
 from __future__ import annotations
 
@@ -20,6 +31,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -31,6 +43,31 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
 DMA_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip"]   # kernels with LDS DMAs
 ARCH = "gfx950"
+VARIANTS = {                       # checking builds: name -> extra defines
+    "racecheck": ["-DATTN_RACE_CHECK=1"],
+    "stamps": ["-DATTN_STAMPS=1"],
+}
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(PKG_DIR, f"libattn_{name}.so")
+
+
+def _jobs() -> int:
+    return max(1, min(8, os.cpu_count() or 1))
+
+
+def _run_all(cmds, verbose=False):
+    """Run compiler commands in parallel; raise on the first failure."""
+    def one(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stderr[-4000:]}")
+        return r
+    with ThreadPoolExecutor(_jobs()) as ex:
+        list(ex.map(one, cmds))
 
 
 def hipcc() -> str:
@@ -60,12 +97,15 @@ def kernel_asm(dma_nop: int, extra=(), cc: str = None) -> str:
     cc = cc or hipcc()
     bdir = os.path.join(PKG_DIR, "_build")
     os.makedirs(bdir, exist_ok=True)
-    text = []
+    outs, cmds = [], []
     for src in DMA_SOURCES:
         out = os.path.join(bdir, f"{os.path.splitext(src)[0]}_nop{dma_nop}.s")
-        cmd = [cc, *compile_flags(extra), f"-DATTN_DMA_NOP={dma_nop}", "-x", "hip", "--cuda-device-only", "-S",
-               os.path.join(CSRC, src), "-o", out]
-        subprocess.run(cmd, check=True, capture_output=True)
+        cmds.append([cc, *compile_flags(extra), f"-DATTN_DMA_NOP={dma_nop}", "-x", "hip", "--cuda-device-only",
+                     "-S", os.path.join(CSRC, src), "-o", out])
+        outs.append(out)
+    _run_all(cmds)
+    text = []
+    for out in outs:
         with open(out) as f:
             text.append(f.read())
     return "\n".join(text)
@@ -88,30 +128,33 @@ def choose_dma_nop(extra=(), cc: str = None, verbose: bool = False) -> int:
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile every HIP/C++ source into ``exact_attention_57_amd/libattn.so``.
+    """Compile every HIP/C++ source into ``exact_attention_57_amd/libattn.so``
+    and the checking builds ``libattn_<variant>.so``.
 
     Always recompiles (it is the "does it build" check).  Objects go to a
-    private build folder; the library is written atomically.
+    private build folder; each library is written atomically.
     """
     cc = hipcc()
-    bdir = os.path.join(PKG_DIR, "_build")
-    os.makedirs(bdir, exist_ok=True)
     nop = choose_dma_nop(extra, cc, verbose)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip", f"-DATTN_DMA_NOP={nop}"] if src.endswith(".hip") else []
-        cmd = [cc, *compile_flags(extra), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    libs = [(LIB_PATH, "main", [f"-DATTN_DMA_NOP={nop}"])]
+    libs += [(variant_path(name), name, ["-DATTN_DMA_NOP=4", *defs]) for name, defs in VARIANTS.items()]
+    cmds, objs = [], {}
+    for path, tag, defs in libs:
+        bdir = os.path.join(PKG_DIR, "_build", tag)
+        os.makedirs(bdir, exist_ok=True)
+        objs[path] = []
+        for src in SOURCES:
+            obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip", *defs] if src.endswith(".hip") else []
+            cmds.append([cc, *compile_flags(extra), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs[path].append(obj)
+    _run_all(cmds, verbose)
+    links = []
+    for path, _, _ in libs:
+        links.append([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", path + ".tmp", *objs[path]])
+    _run_all(links, verbose)
+    for path, _, _ in libs:
+        os.replace(path + ".tmp", path)
     return LIB_PATH
 
 

@@ -142,6 +142,16 @@ __device__ __forceinline__ void decode_block(const BwdParams& p, bool reverse, i
 template <bool V>
 struct GroupTag { static constexpr bool value = V; };
 
+// Workgroup barrier; in the race-check build (ATTN_RACE_CHECK, see
+// attn_fwd_common.h) every memory access of the wave is drained first and the
+// barrier is passed twice.
+__device__ __forceinline__ void block_sync() {
+  __syncthreads();
+#if ATTN_RACE_CHECK && defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+}
+
 // Row sigma(m): m with bits 2 and 3 swapped.
 __device__ __forceinline__ int sigma(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -346,7 +356,7 @@ void bwd_dq_kernel(BwdParams p) {
     tile_load<DV>(vr, vbase, v_stride, t * kTile, L, tid);
     tile_store<DQK, true, true>(kr, k_row, k_tr, tid);
     tile_store<DV, true, false>(vr, v_row, v_row, tid);
-    __syncthreads();
+    block_sync();
     const int k0 = t * kTile;
     const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
 #pragma unroll
@@ -386,7 +396,7 @@ void bwd_dq_kernel(BwdParams p) {
           dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
       }
     }
-    __syncthreads();
+    block_sync();
   }
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
@@ -772,10 +782,10 @@ void bwd_dkdv_split_kernel(BwdParams p) {
       stage_tile(1);
     }
     if (!Q_ONCE && ntiles > 2) load_tile(2);
-    __syncthreads();
+    block_sync();
     half_a(0);
     for (int nb = 0; nb < nblk; ++nb) {
-      __syncthreads();
+      block_sync();
       if (nb % QB == 0 && nb >= QB) {
         const int u = nb / QB;
         if (u + 1 < ntiles) {
@@ -787,7 +797,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
       half_b(nb);
       if (nb + 1 < nblk) half_a(nb + 1);
     }
-    __syncthreads();                           // the staging area overlaps the tile buffers
+    block_sync();                           // the staging area overlaps the tile buffers
     lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
     if constexpr (KG) {
       f32x16_t dk[KBLK];

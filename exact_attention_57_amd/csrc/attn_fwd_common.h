@@ -19,6 +19,20 @@
 #ifndef ATTN_SETPRIO
 #define ATTN_SETPRIO 1  // issue priority of the wave in its matrix phase (0: no change)
 #endif
+// Race-check build (1): every workgroup barrier first waits for all of the
+// wave's memory traffic (LDS DMAs and LDS reads included) and is passed
+// twice, so no DMA, LDS access or phase overlaps a barrier.  Its outputs must
+// equal the default build's bit for bit; a tile read before its DMA landed, or
+// a buffer refilled while still being read, would make them differ.
+#ifndef ATTN_RACE_CHECK
+#define ATTN_RACE_CHECK 0
+#endif
+// Instrumented build (1): the forward kernels write a timing record per
+// workgroup after the four counters of attn_fwd_opts.stats (real-time start
+// and end, hardware ids, per-phase cycle sums; see attn_fwd_kernel.hip).
+#ifndef ATTN_STAMPS
+#define ATTN_STAMPS 0
+#endif
 
 namespace attn {
 
@@ -177,7 +191,11 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t nbytes) 
 // another iteration.
 __device__ __forceinline__ void barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
+#if ATTN_RACE_CHECK
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
+#else
   asm volatile("s_barrier" ::: "memory");
+#endif
 #endif
 }
 // Wait until at most N of this wave's DMAs are in flight, then barrier: the
@@ -186,7 +204,11 @@ __device__ __forceinline__ void barrier() {
 template <int N>
 __device__ __forceinline__ void dma_wait_barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
+#if ATTN_RACE_CHECK
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
+#else
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+#endif
 #endif
 }
 __device__ __forceinline__ void dma_wait_all() {
@@ -194,6 +216,34 @@ __device__ __forceinline__ void dma_wait_all() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #endif
 }
+
+// Clocks of the instrumented build: s_memtime counts shader clock cycles,
+// s_memrealtime a constant-rate (100 MHz) clock common to the whole chip.
+__device__ __forceinline__ uint64_t cycles_now() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_s_memtime();
+#else
+  return 0;
+#endif
+}
+__device__ __forceinline__ uint64_t realtime_now() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_s_memrealtime();
+#else
+  return 0;
+#endif
+}
+// (XCC id << 32) | HW_ID (CU, SIMD, shader array and engine of this wave)
+__device__ __forceinline__ uint64_t hardware_ids() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));    // HW_REG_HW_ID, 32 bits
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));  // HW_REG_XCC_ID, 16 bits
+  return ((uint64_t)xcc << 32) | hw;
+#else
+  return 0;
+#endif
+}
+constexpr int kStampWords = 16;   // uint64 per workgroup record of the instrumented build
 
 struct True { static constexpr bool value = true; };
 struct False { static constexpr bool value = false; };

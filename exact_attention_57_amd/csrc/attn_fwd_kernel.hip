@@ -146,6 +146,27 @@ void attn_fwd_kernel(FwdParams p) {
   const int g = lane / 32;       // lane half
   const int lq = lane % 32;      // query column
 
+  // Instrumented build: a record of kStampWords uint64 per workgroup after
+  // the four counters of p.stats (when given), at the workgroup's linear grid
+  // index:
+  //   [0] real-time clock at entry, [1] at the end (wave 0; 100 MHz),
+  //   [2] (XCC id << 32) | HW_ID of wave 0, [3] work item (h << 40 | b << 20 | query block),
+  //   [4] tile-loop iterations, [5..7] wave 0's shader cycles in the prologue,
+  //   the tile loop and the epilogue, [8..11] wave 0's cycles summed over the
+  //   loop in its matrix phases, the barrier after them, its softmax phases
+  //   (with the operand prefetch) and the barrier after those, [12..15] the
+  //   same for wave 4 (the other group on the same SIMD).
+  // The stamps wait for the counter reads, so this build runs a little slower.
+#if ATTN_STAMPS
+  const uint64_t rt_start = realtime_now();
+  const uint64_t cy_start = cycles_now();
+  uint64_t ph[4] = {0, 0, 0, 0};
+  uint64_t cy_loop0 = 0, cy_loop1 = 0;
+  unsigned long long* const rec =
+      p.stats ? p.stats + 4 + (int64_t)kStampWords * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z))
+              : nullptr;
+#endif
+
   // ---- work decode.  Longest-first schedule: a 1-D grid whose workgroups
   // the hardware deals to the 8 XCDs in turn (workgroup i to XCD i mod 8).
   // XCD x takes a contiguous run of a list ordered by (sequence, head) pair,
@@ -183,7 +204,18 @@ void attn_fwd_kernel(FwdParams p) {
   seq_range(b, seq0, L);
   const int T = p.cu_seqlens ? p.cu_seqlens[p.B] : p.B * p.N;
   const int q0 = qblk * kBlockM;
-  if (q0 >= L) return;  // uniform over the workgroup
+  if (q0 >= L) {  // uniform over the workgroup
+#if ATTN_STAMPS
+    if (rec && tid == 0) {
+      rec[0] = rt_start;
+      rec[1] = realtime_now();
+      rec[2] = hardware_ids();
+      rec[3] = ((uint64_t)h << 40) | ((uint64_t)b << 20) | (uint64_t)qblk;
+      for (int i = 4; i < kStampWords; ++i) rec[i] = 0;
+    }
+#endif
+    return;
+  }
   const int kend = CAUSAL ? min(L, q0 + kBlockM) : L;
   const int ntiles = (kend + BN - 1) / BN;
 
@@ -623,24 +655,39 @@ void attn_fwd_kernel(FwdParams p) {
       const int bm1 = (b0 == 0) ? 2 : b0 - 1;    // (j - 1) mod 3 = (j + 2) mod 3
       const int bp1 = (b0 == 2) ? 0 : b0 + 1;    // (j + 1) mod 3
       const int vc = j & 1, vp = vc ^ 1;         // V buffers of V[j] and V[j-1]
+#if ATTN_STAMPS
+      uint64_t c0 = cycles_now(), c1;
+#define ATTN_PHASE(i) (c1 = cycles_now(), ph[i] += c1 - c0, c0 = c1)
+#else
+#define ATTN_PHASE(i) ((void)0)
+#endif
       if (G == 0) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
         matrix(True{}, vbuf(vp), kbuf(b0), k_tile(t_n2), v_tile(t_cur), kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        ATTN_PHASE(0);
         dma_wait_barrier<Lay::ISSUES>();         // K[j+1] has landed
+        ATTN_PHASE(1);
         if (j < nact) softmax(t_cur);
         prefetch(vbuf(vc), kbuf(bp1));           // operands of matrix(j+1)
+        ATTN_PHASE(2);
         dma_wait_barrier<Lay::K_ISSUES>();       // V[j] has landed
+        ATTN_PHASE(3);
       } else {
         if (prefetch_next && j == nact - 1) prefetch_l2(kbuf(bm1));
         if (j >= 1 && j - 1 < nact) softmax(t_prev);
         prefetch(vbuf(vp), kbuf(b0));            // operands of matrix(j)
+        ATTN_PHASE(2);
         barrier();
+        ATTN_PHASE(3);
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
         matrix(False{}, vbuf(vp), kbuf(b0), 0u, 0u, kbuf(bm1), vbuf(vc));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        ATTN_PHASE(0);
         barrier();
+        ATTN_PHASE(1);
       }
+#undef ATTN_PHASE
       n_tiles += (j < nact && (SPARSE || j <= t_last)) ? 1u : 0u;
       b0 = bp1;
       t_prev = t_cur;
@@ -662,9 +709,15 @@ void attn_fwd_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #endif
+#if ATTN_STAMPS
+  cy_loop0 = cycles_now();
+#endif
   if (grp == 0) run(Grp0{});
   else run(Grp1{});
   dma_wait_all();   // the last iteration's DMAs land before the LDS is reused
+#if ATTN_STAMPS
+  cy_loop1 = cycles_now();
+#endif
 
   // ---- epilogue: O = O^T / l (bf16), LSE = (m + log2 l) ln 2.  A lane holds
   // its query row's outputs in 8-byte pieces, so storing from registers would
@@ -701,6 +754,23 @@ void attn_fwd_kernel(FwdParams p) {
   if (row_valid && g == 0)
     p.lse[(int64_t)h * T + seq0 + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.693147180559945309f;
 
+#if ATTN_STAMPS
+  if (rec && lane == 0) {
+    if (wave == 0) {
+      rec[0] = rt_start;
+      rec[2] = hardware_ids();
+      rec[3] = ((uint64_t)h << 40) | ((uint64_t)b << 20) | (uint64_t)qblk;
+      rec[4] = (uint64_t)nact + 1;
+      rec[5] = cy_loop0 - cy_start;
+      rec[6] = cy_loop1 - cy_loop0;
+      rec[7] = cycles_now() - cy_loop1;
+      for (int i = 0; i < 4; ++i) rec[8 + i] = ph[i];
+      rec[1] = realtime_now();
+    } else if (wave == kWaves / 2) {
+      for (int i = 0; i < 4; ++i) rec[12 + i] = ph[i];
+    }
+  }
+#endif
   if (p.stats) {
     // wave totals -> one atomic per counter per wave
     if (lane == 0) {
