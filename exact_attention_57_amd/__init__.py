@@ -17,7 +17,7 @@ import os
 __all__ = [
     "AttnError", "lib", "fwd", "fwd_raw", "fwd_fp8", "fwd_fp8_raw", "bwd", "bwd_raw", "debug_exp2", "strerror", "version", "geometry",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_ALIGN",
-    "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
+    "ATTN_ERR_VALUE", "ATTN_ERR_LAUNCH", "ATTN_ERR_SCRATCH", "NOALLOC_MAX_ROWS", "bwd_noalloc", "bwd_noalloc_raw", "SCHEDULE_LONGEST_FIRST", "SCHEDULE_NATURAL",
     "SUPPORTED_DIMS", "BWD_SUPPORTED_DIMS", "FP8_SUPPORTED_DIMS", "LIB_PATH", "CHECK_BUILDS", "check_build",
 ]
 
@@ -31,6 +31,8 @@ ATTN_ERR_UNSUPPORTED = -3
 ATTN_ERR_ALIGN = -4
 ATTN_ERR_VALUE = -5
 ATTN_ERR_LAUNCH = -6
+ATTN_ERR_SCRATCH = -7
+NOALLOC_MAX_ROWS = 16 * 1024 * 1024      # H * B * N limit of attn_bwd_noalloc
 SCHEDULE_LONGEST_FIRST = 0
 SCHEDULE_NATURAL = 1
 SUPPORTED_DIMS = ((64, 64), (128, 128), (192, 128))
@@ -94,6 +96,8 @@ def _load(path=LIB_PATH):
     L.attn_fwd_fp8.restype = i32
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_bwd.restype = i32
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_bwd_noalloc.restype = i32
     L.attn_strerror.argtypes = [i32]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_debug_exp2.argtypes = [vp, vp, i32, i32, vp]
@@ -373,6 +377,62 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens=None, *, max_seqlen=None, causal=False
                  B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream), _lib=_lib)
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc_raw(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, cu_ptr,
+                    B, H, N, d_qk, d_v, scale, causal, stream) -> int:
+    """Call attn_bwd_noalloc with raw integer pointers; returns the status code."""
+    return int(lib.attn_bwd_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, cu_ptr,
+                                    int(B), int(H), int(N), int(d_qk), int(d_v), float(scale), int(bool(causal)),
+                                    stream))
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens=None, *, max_seqlen=None, causal=False, scale=None,
+                stream=None):
+    """The backward pass without any allocation (attn_bwd_noalloc): as ``bwd``,
+    but the caller passes dq, dk, dv, and the D workspace is the library's
+    static scratch array (H * B * N <= NOALLOC_MAX_ROWS).  Calls that overlap
+    in time on one GPU share that array and must not be issued.  Returns
+    (dq, dk, dv)."""
+    import torch
+    if q.dim() == 4:
+        B, N, H, d_qk = q.shape
+        if cu_seqlens is not None:
+            raise ValueError("4-D inputs are fixed length; pass [T, H, d] with cu_seqlens")
+    elif q.dim() == 3:
+        T, H, d_qk = q.shape
+        if cu_seqlens is None:
+            N = T if max_seqlen is None else int(max_seqlen)
+            if N <= 0 or T % N:
+                raise ValueError("fixed-length [T, H, d] input needs T = B * max_seqlen")
+            B = T // N
+        else:
+            if max_seqlen is None:
+                raise ValueError("packed input needs max_seqlen")
+            B = cu_seqlens.numel() - 1
+            N = int(max_seqlen)
+    else:
+        raise ValueError("q must be [B, N, H, d] or [T, H, d]")
+    d_v = v.shape[-1]
+    T = B * N if q.dim() == 4 else q.shape[0]
+    dev = _check_inputs((("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), (torch.bfloat16,), "bwd_noalloc")
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or o.shape != v.shape or dout.shape != v.shape:
+        raise ValueError("q, k, v, o, dout shapes disagree")
+    _check_tensor("lse", lse, (torch.float32,), dev, shape=(H, T))
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev, shape=(B + 1,))
+    _check_tensor("dq", dq, (torch.bfloat16,), dev, shape=q.shape)
+    _check_tensor("dk", dk, (torch.bfloat16,), dev, shape=k.shape)
+    _check_tensor("dv", dv, (torch.bfloat16,), dev, shape=v.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    st = bwd_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                         B, H, N, d_qk, d_v, scale, causal, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

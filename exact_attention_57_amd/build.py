@@ -40,7 +40,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip", "attn_scratch.hip", "attn_api.cpp"]
 DMA_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip"]   # kernels with LDS DMAs
 ARCH = "gfx950"
 VARIANTS = {                       # checking builds: name -> extra defines

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "attn_api_internal.h"
 #include "attn_bwd_kernel.h"
 #include "attn_fwd_kernel.h"
 
@@ -27,6 +28,60 @@ bool supported_dims(int d_qk, int d_v) {
 
 }  // namespace
 
+namespace attn_internal {
+
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              const void* dq, const void* dk, const void* dv, const float* delta, bool with_delta,
+              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v, float scale) {
+  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
+  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (N == 0) return kNothingToDo;  // no tokens: nothing to do
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (with_delta && !delta)) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || (with_delta && !aligned(delta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+    return ATTN_ERR_ALIGN;
+  const int rows = attn_grad::block_rows();
+  const int64_t nb = ((int64_t)N + rows - 1) / rows;
+  if ((int64_t)H * B * nb > INT32_MAX) return ATTN_ERR_SHAPE;   // one workgroup per (sequence, head, block)
+  if ((int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;        // token indices are 32-bit in the kernels
+  if ((int64_t)B * N * H > INT32_MAX) return ATTN_ERR_SHAPE;    // rows of the D pass
+  // one sequence's Q, K, V or dO rows of one head are addressed through a
+  // 32-bit buffer range, with tile requests up to 255 rows past its end
+  if (((int64_t)N + 256) * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, float* delta, const int32_t* cu_seqlens, int B, int H, int N,
+               int d_qk, int d_v, float scale, int causal, hipStream_t stream) {
+  const int rows = attn_grad::block_rows();
+  attn_grad::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.delta = delta;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_blocks = (int)(((int64_t)N + rows - 1) / rows);
+  p.scale = scale;
+  p.c = scale * 1.44269504088896340736f;
+  const hipError_t err = attn_grad::launch_bwd(p, d_qk, d_v, causal != 0, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace attn_internal
+
 extern "C" {
 
 void attn_fwd_opts_default(attn_fwd_opts* opts) {
@@ -47,6 +102,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes; lse, cu_seqlens 4 bytes";
     case ATTN_ERR_VALUE: return "invalid value: non-finite scale or option out of range";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ATTN_ERR_SCRATCH: return "too large for the allocation-free entry point: H*B*N above ATTN_NOALLOC_MAX_ROWS";
     default: return "unknown attn status";
   }
 }
@@ -188,44 +244,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream) {
-  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_SHAPE;
-  if (!supported_dims(d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return ATTN_ERR_VALUE;
-  if (N == 0) return ATTN_OK;  // no tokens: nothing to do
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-    return ATTN_ERR_ALIGN;
-  if (!aligned(lse, 4) || !aligned(delta, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return ATTN_ERR_ALIGN;
-  const int rows = attn_grad::block_rows();
-  const int64_t nb = ((int64_t)N + rows - 1) / rows;
-  if ((int64_t)H * B * nb > INT32_MAX) return ATTN_ERR_SHAPE;   // one workgroup per (sequence, head, block)
-  if ((int64_t)B * N > INT32_MAX) return ATTN_ERR_SHAPE;        // token indices are 32-bit in the kernels
-  if ((int64_t)B * N * H > INT32_MAX) return ATTN_ERR_SHAPE;    // rows of the D pass
-  // one sequence's Q, K, V or dO rows of one head are addressed through a
-  // 32-bit buffer range, with tile requests up to 255 rows past its end
-  if (((int64_t)N + 256) * H * (d_qk > d_v ? d_qk : d_v) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
-
-  attn_grad::BwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<const uint16_t*>(o);
-  p.dout = static_cast<const uint16_t*>(dout);
-  p.lse = lse;
-  p.dq = static_cast<uint16_t*>(dq);
-  p.dk = static_cast<uint16_t*>(dk);
-  p.dv = static_cast<uint16_t*>(dv);
-  p.delta = delta;
-  p.cu_seqlens = cu_seqlens;
-  p.B = B;
-  p.H = H;
-  p.N = N;
-  p.n_blocks = (int)nb;
-  p.scale = scale;
-  p.c = scale * 1.44269504088896340736f;
-  const hipError_t err = attn_grad::launch_bwd(p, d_qk, d_v, causal != 0, stream);
-  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  const int st = attn_internal::bwd_check(q, k, v, o, dout, lse, dq, dk, dv, delta, true, cu_seqlens, B, H, N,
+                                          d_qk, d_v, scale);
+  if (st != ATTN_OK) return st == attn_internal::kNothingToDo ? ATTN_OK : st;
+  return attn_internal::bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, cu_seqlens, B, H, N, d_qk, d_v,
+                                   scale, causal, stream);
 }
 
 int attn_debug_exp2(const float* x, float* y, int n, int use_poly, hipStream_t stream) {

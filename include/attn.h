@@ -80,7 +80,8 @@ typedef enum attn_status {
   ATTN_ERR_UNSUPPORTED = -3,  /* (d_qk, d_v) not one of the supported pairs */
   ATTN_ERR_ALIGN = -4,        /* pointer misaligned */
   ATTN_ERR_VALUE = -5,        /* non-finite scale or invalid option value */
-  ATTN_ERR_LAUNCH = -6        /* the HIP launch failed */
+  ATTN_ERR_LAUNCH = -6,       /* the HIP launch failed */
+  ATTN_ERR_SCRATCH = -7       /* larger than attn_bwd_noalloc's scratch array holds */
 } attn_status;
 
 /* Schedules for the (sequence, head, query-block) work items. */
@@ -181,6 +182,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
              float scale, int causal, hipStream_t stream);
+
+/* Allocation-free backward pass, for callers that cannot allocate device
+ * memory (work under stream capture, serving loops or harnesses that forbid
+ * allocation): attn_bwd with the same arguments except `delta`.  The D
+ * workspace lives in a static device array of the library (64 MiB, held by
+ * every GPU the library runs on until the process ends), so the call
+ * allocates nothing; it needs H * B * N <= ATTN_NOALLOC_MAX_ROWS, else
+ * ATTN_ERR_SCRATCH (checked, like every other argument, before any HIP
+ * call).  All calls on one GPU share its array: calls that overlap in time on
+ * the same GPU (other streams or threads) race on it and must not be issued.
+ * The first call on a device looks the array's address up (hipGetSymbolAddress,
+ * no allocation); ATTN_ERR_LAUNCH if that fails.  Results are attn_bwd's
+ * bit for bit (the same kernels). */
+#define ATTN_NOALLOC_MAX_ROWS (16 * 1024 * 1024)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     const int32_t* cu_seqlens, int B, int H, int N, int d_qk, int d_v,
+                     float scale, int causal, hipStream_t stream);
 
 /* FP8 forward pass: attention of E4M3 inputs with per-tensor dequantisation
  * factors.  The pages name FP8 as the low-precision arithmetic of the Hopper

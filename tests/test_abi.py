@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("attn_fwd", "attn_fwd_ex", "attn_fwd_opts_default", "attn_strerror",
-                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry", "attn_bwd", "attn_fwd_fp8"):
+                 "attn_debug_exp2", "attn_version", "attn_fwd_geometry", "attn_bwd", "attn_fwd_fp8",
+                 "attn_bwd_noalloc"):
         assert want in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_code():
     codes = [ea.ATTN_OK, ea.ATTN_ERR_NULL, ea.ATTN_ERR_SHAPE, ea.ATTN_ERR_UNSUPPORTED,
-             ea.ATTN_ERR_ALIGN, ea.ATTN_ERR_VALUE, ea.ATTN_ERR_LAUNCH]
+             ea.ATTN_ERR_ALIGN, ea.ATTN_ERR_VALUE, ea.ATTN_ERR_LAUNCH, ea.ATTN_ERR_SCRATCH]
     msgs = [ea.strerror(c) for c in codes]
     assert all(msgs) and len(set(msgs)) == len(msgs)
     assert "unknown" in ea.strerror(-99)
@@ -218,3 +219,37 @@ def call_fp8(**kw):
 ])
 def test_fp8_validation_codes(kw, code):
     assert call_fp8(**kw) == code
+
+
+def call_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, cu=None, B=1, H=1, N=1, d_qk=128, d_v=128,
+                scale=1.0, causal=0, stream=None)
+    args.update(kw)
+    return ea.bwd_noalloc_raw(args["q"], args["k"], args["v"], args["o"], args["do"], args["lse"], args["dq"],
+                              args["dk"], args["dv"], args["cu"], args["B"], args["H"], args["N"], args["d_qk"],
+                              args["d_v"], args["scale"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), ea.ATTN_ERR_SHAPE),
+    (dict(d_qk=96, d_v=96), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), ea.ATTN_ERR_VALUE),
+    (dict(dk=None), ea.ATTN_ERR_NULL),
+    (dict(do=P + 8), ea.ATTN_ERR_ALIGN),
+    (dict(lse=P + 2), ea.ATTN_ERR_ALIGN),
+    (dict(N=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None), ea.ATTN_OK),
+    # the scratch array holds ATTN_NOALLOC_MAX_ROWS rows of D (H * B * N)
+    (dict(H=16, B=2, N=ea.NOALLOC_MAX_ROWS // 32 + 1), ea.ATTN_ERR_SCRATCH),
+    (dict(H=1, B=1, N=ea.NOALLOC_MAX_ROWS + 1, d_qk=64, d_v=64), ea.ATTN_ERR_SCRATCH),
+])
+def test_noalloc_validation_codes(kw, code):
+    """The allocation-free backward entry point checks its arguments like
+    attn_bwd, and rejects problems whose D rows exceed its scratch array,
+    before any HIP call."""
+    assert call_noalloc(**kw) == code
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_MAX_ROWS \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == ea.NOALLOC_MAX_ROWS
