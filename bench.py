@@ -316,6 +316,9 @@ def main():
                     help="time the instrumented build (libattn_stamps.so) of the bf16 forward pass and summarise "
                          "its per-workgroup records: dispatch order, XCD mapping, per-CU balance, finish tail, "
                          "cycles per phase")
+    ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
+                    help="only time the vendor library's bf16 GEMM (torch.matmul, N x N x N, fp32 accumulation) "
+                         "with --warmup and --steps launches, as a practical matrix-core ceiling on this chip")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
@@ -330,6 +333,28 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.gemm_ceiling:
+        n = args.gemm_ceiling
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=gen)
+        b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=gen)
+        c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.warmup):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_ceiling": f"torch.matmul bf16 {n}x{n}x{n}", "steps": args.steps,
+                          "warmup": args.warmup, "kernel_ms": round(ms, 4), "tflops": round(tf, 1),
+                          "pct_of_dense_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
