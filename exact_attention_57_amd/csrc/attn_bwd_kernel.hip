@@ -573,7 +573,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   // layout, and the transposed reads take that layout's bank conflicts
   constexpr bool Q_ONCE = DQK > 128;
   constexpr int QS = (Q_ONCE ? 1 : 2) * Q_ELEMS;                       // Q elements stored per tile
-  constexpr int TILE_ELEMS = QS + 2 * O_ELEMS + 2 * kTile * 2;          // + LSE (log2 units), D
+  // + LSE (log2 units) and D as fp32, padded to whole 1 KB blocks
+  constexpr int TILE_ELEMS = (QS + 2 * O_ELEMS + 2 * kTile * 2 + 511) / 512 * 512;
   constexpr int P_ELEMS = kWaves * kWave * 16;                          // 32 x 32 bf16 per dV wave
   constexpr int STAGE_ELEMS = 2 * kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
   constexpr int WORK_ELEMS = 2 * TILE_ELEMS + 2 * P_ELEMS;
@@ -612,25 +613,54 @@ void bwd_dkdv_split_kernel(BwdParams p) {
 
   const f32x16_t zero = {};
 
-  TileRegs<DQK, kThreads2> qr;
-  TileRegs<DV, kThreads2> dr;
-  // threads 0..63: LSE, 64..127: D.  The LSE goes to log2 units only when it
-  // is staged: an arithmetic use right after the load would make the wave wait
-  // for every load in flight, the next tile's included.
+  auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
+  // Q and dO tiles are copied HBM/L2 -> LDS by buffer_load ... lds, every wave
+  // issuing its share of the tile's 1 KB requests: the Q rows in the row
+  // layout (and, up to d_qk = 128, again in the transposed layout) and the dO
+  // rows in both layouts.  Request lane i writes the 16 bytes at LDS position
+  // 8 i of its block, i.e. chunk `pos` of row `row`, which holds the tile's
+  // chunk pos ^ f(row) of that row.  The buffer ranges end after row L-1 of
+  // the sequence, so rows past its end read as zeros.
+  constexpr int Q_REQ = Q_ELEMS / 512, O_REQ = O_ELEMS / 512;   // 1 KB requests per copy
+  constexpr int NQCOPY = Q_ONCE ? 1 : 2;
+  constexpr int REQ = NQCOPY * Q_REQ + 2 * O_REQ;
+  static_assert(Q_ELEMS % 512 == 0 && O_ELEMS % 512 == 0 && REQ % (2 * kWaves) == 0, "request split");
+  constexpr int REQ_W = REQ / (2 * kWaves);                      // requests per wave per tile
+  const uint32_t q_rowbytes = (uint32_t)(qk_stride * 2), o_rowbytes = (uint32_t)(v_stride * 2);
+  const attn::u32x4_t q_rsrc = attn::make_rsrc(qbase, (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
+  const attn::u32x4_t o_rsrc = attn::make_rsrc(dobase, (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
+  auto issue_tile = [&] __device__ (int t) __attribute__((always_inline)) {
+    lds_u16_t* const base = buf(t);
+    const uint32_t q0t = (uint32_t)(qstart + t * kTile);
+#pragma unroll
+    for (int i = 0; i < REQ_W; ++i) {
+      const int r = wave * REQ_W + i;                            // uniform
+      const bool isq = r < NQCOPY * Q_REQ;
+      const int copy = isq ? r / Q_REQ : 2 + (r - NQCOPY * Q_REQ) / O_REQ;   // 0, 1: Q row, tr; 2, 3: dO row, tr
+      const int rr = isq ? r % Q_REQ : (r - NQCOPY * Q_REQ) % O_REQ;
+      const int D = isq ? DQK : DV;
+      const int e = rr * 512 + 8 * lane;                         // element of the copy (row-major, D per row)
+      const int row = e / D, pos = (e % D) / 8;
+      const int f = copy == 0 ? RowSwz<DQK>::f(row)
+                  : copy == 1 ? TrSwz<DQK>::f(row)
+                  : copy == 2 ? RowSwz<DV>::f(row) : TrSwz<DV>::f(row);
+      const uint32_t rowbytes = isq ? q_rowbytes : o_rowbytes;
+      const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
+      lds_u16_t* const dst = base + (copy == 0 ? 0 : copy == 1 ? Q_ELEMS : copy == 2 ? QS : QS + O_ELEMS) + rr * 512;
+      attn::dma_chunk(isq ? q_rsrc : o_rsrc, lane_off, q0t * rowbytes, dst);
+    }
+  };
+  // LSE and D of a tile's 64 rows go through registers (threads 0..63: LSE,
+  // 64..127: D), loaded one tile ahead.  The LSE goes to log2 units only when
+  // it is staged: an arithmetic use right after the load would make the wave
+  // wait for every load in flight.
   float rowval = 0.0f;
-  auto load_tile = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int q0t = qstart + t * kTile;
-    tile_load<DQK, kThreads2>(qr, qbase, qk_stride, q0t, L, tid);
-    tile_load<DV, kThreads2>(dr, dobase, v_stride, q0t, L, tid);
-    const int r = q0t + (tid % kTile);
+  auto load_rows = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int r = qstart + t * kTile + (tid % kTile);
     if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] : d_h[r]) : 0.0f;
   };
-  auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
-  auto stage_tile = [&] __device__ (int t) __attribute__((always_inline)) {
-    lds_u16_t* const base = buf(t);
-    tile_store<DQK, true, !Q_ONCE, kThreads2>(qr, base, base + Q_ELEMS, tid);
-    tile_store<DV, true, true, kThreads2>(dr, base + QS, base + QS + O_ELEMS, tid);
-    if (tid < 2 * kTile) ((lds_f32_t*)(base + QS + 2 * O_ELEMS))[tid] = tid < kTile ? rowval * kLog2e : rowval;
+  auto stage_rows = [&] __device__ (int t) __attribute__((always_inline)) {
+    if (tid < 2 * kTile) ((lds_f32_t*)(buf(t) + QS + 2 * O_ELEMS))[tid] = tid < kTile ? rowval * kLog2e : rowval;
   };
   // this lane's 32 bytes of the P block of key slice wv, buffer i
   auto pslot = [&] __device__ (int i) __attribute__((always_inline)) {
@@ -770,32 +800,35 @@ void bwd_dkdv_split_kernel(BwdParams p) {
     };
 
     // Tiles: both buffers filled up front; tile u+1 goes into the buffer of tile
-    // u-1 after barrier 2u (u >= 1), when every wave has finished block 2u-1,
-    // and is visible from barrier 2u+1 on, before block 2u+2 reads it.  Its
-    // global loads are issued one tile ahead into registers, except at
-    // d_qk = 192 (Q_ONCE), where those registers are not available and the
-    // tile is loaded right before it is staged.
-    load_tile(0);
-    stage_tile(0);
+    // u-1 after barrier 2u (u >= 1), when every wave has finished block 2u-1:
+    // its DMAs are issued right after that barrier and awaited before the next
+    // one, so it is visible from barrier 2u+1 on, before block 2u+2 reads it.
+    // The LSE and D rows follow the same schedule through registers, their
+    // loads one tile ahead.
+    issue_tile(0);
+    load_rows(0);
+    stage_rows(0);
     if (ntiles > 1) {
-      load_tile(1);
-      stage_tile(1);
+      issue_tile(1);
+      load_rows(1);
+      stage_rows(1);
     }
-    if (!Q_ONCE && ntiles > 2) load_tile(2);
+    if (ntiles > 2) load_rows(2);
+    attn::dma_wait_all();
     block_sync();
     half_a(0);
     for (int nb = 0; nb < nblk; ++nb) {
       block_sync();
-      if (nb % QB == 0 && nb >= QB) {
+      const bool refill = nb % QB == 0 && nb >= QB && nb / QB + 1 < ntiles;
+      if (refill) {
         const int u = nb / QB;
-        if (u + 1 < ntiles) {
-          if (Q_ONCE) load_tile(u + 1);
-          stage_tile(u + 1);
-          if (!Q_ONCE && u + 2 < ntiles) load_tile(u + 2);
-        }
+        stage_rows(u + 1);
+        if (u + 2 < ntiles) load_rows(u + 2);
+        issue_tile(u + 1);
       }
       half_b(nb);
       if (nb + 1 < nblk) half_a(nb + 1);
+      if (refill) attn::dma_wait_all();        // tile u+1 has landed before the next barrier
     }
     block_sync();                           // the staging area overlaps the tile buffers
     lds_u16_t* const stage = lds + wave * kRows * ((DQK > DV ? DQK : DV) + 8);
