@@ -77,9 +77,12 @@ int block_rows() { return kBlock; }
 // LDS layouts of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
 // bytes): chunk c of row r sits at position c ^ f(r).
 //  * row layout, read 16 bytes per lane with 16 consecutive rows per
-//    quarter-wave: f(r) = r mod 16 (R = 16), (r/2) mod 8 (R = 8 or 24: two
-//    rows share a 64-bank window, or a row of 24 chunks starts on alternate
-//    halves of it);
+//    quarter-wave: f(r) = r mod 16 (R = 16); for R = 8 or 24 a row starts on
+//    alternate halves of the 64 banks, so the 4-bank group of chunk c of row r
+//    is (c ^ f(r) ^ 8 (r mod 2)) mod 16, and f(r) = 4 b1(r) + (r/4) mod 4 (bits
+//    of r/2 rotated) gives the 16 rows of a quarter-wave distinct groups and,
+//    since bit 2 of f follows b1(r), the 4 rows x 4 chunks of a transposing read
+//    from this layout (at (192, 128) the Q tile is stored only in it) too;
 //  * transposed layout, read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
 //    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8 or 24).
 // Both are invariant under a shift of r by a multiple of 16, and keep a chunk
@@ -87,7 +90,7 @@ int block_rows() { return kBlock; }
 template <int D>
 struct RowSwz {
   static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
-  __device__ static int f(int r) { return (D == 128) ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int f(int r) { return (D == 128) ? (r & 15) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)); }
 };
 template <int D>
 struct TrSwz {
@@ -211,8 +214,7 @@ __device__ __forceinline__ void tile_store(const TileRegs<D, NT>& t, lds_u16_t* 
 // k-step s: 8 columns from 16 s + 8 g); transposed reads (A operand: columns
 // db*32 + (lane % 32) at 8 consecutive rows from 8 g, as two 4-row reads),
 // from a tile in the transposed layout, or in the row layout when TR_ROW
-// (a tile stored once for both kinds of read: correct, with 2-way bank
-// conflicts on the transposed reads).
+// (a tile stored once for both kinds of read).
 template <int D, bool TR_ROW = false>
 struct Reads {
   int row[D / 16];
@@ -570,7 +572,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
   // Q is read row-wise (S) and transposed (dK); at d_qk = 192 two copies of
   // two buffers would not fit in LDS, so the tile is stored once, in the row
-  // layout, and the transposed reads take that layout's bank conflicts
+  // layout, which serves both reads without bank conflicts
   constexpr bool Q_ONCE = DQK > 128;
   constexpr int QS = (Q_ONCE ? 1 : 2) * Q_ELEMS;                       // Q elements stored per tile
   // + LSE (log2 units) and D as fp32, padded to whole 1 KB blocks
@@ -662,9 +664,12 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   auto stage_rows = [&] __device__ (int t) __attribute__((always_inline)) {
     if (tid < 2 * kTile) ((lds_f32_t*)(buf(t) + QS + 2 * O_ELEMS))[tid] = tid < kTile ? rowval * kLog2e : rowval;
   };
-  // this lane's 32 bytes of the P block of key slice wv, buffer i
+  // this lane's 32 bytes of the P block of key slice wv, buffer i, as two
+  // 16-byte halves P_HALF apart: each half of all lanes is contiguous, so the
+  // 16 lanes of a pass cover the 64 banks once
+  constexpr int P_HALF = P_ELEMS / 2 / 8;                              // in 16-byte units
   auto pslot = [&] __device__ (int i) __attribute__((always_inline)) {
-    return (lds_u32x4_t*)(lds + 2 * TILE_ELEMS + i * P_ELEMS + (wv * kWave + lane) * 16);
+    return (lds_u32x4_t*)(lds + 2 * TILE_ELEMS + i * P_ELEMS + (wv * kWave + lane) * 8);
   };
 
   // Each group runs the same loop (and the same barriers) with its own
@@ -744,7 +749,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
         }
         lds_u32x4_t* const slot = pslot(nb & 1);
         slot[0] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
-        slot[1] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
+        slot[P_HALF] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
       } else {
         bf16x8_t a_p[V_STEPS];
   #pragma unroll
@@ -776,7 +781,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
       } else {
         const lds_f32_t* const d_s = (const lds_f32_t*)(base + QS + 2 * O_ELEMS) + kTile;
         const lds_u32x4_t* const slot = pslot(nb & 1);
-        const u32x4_t praw[2] = {slot[0], slot[1]};
+        const u32x4_t praw[2] = {slot[0], slot[P_HALF]};
   #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           uint32_t dsb[4];
