@@ -416,6 +416,9 @@ void bwd_dq_kernel(BwdParams p) {
 #ifndef ATTN_BWD_DQ_DMA
 #define ATTN_BWD_DQ_DMA 1   // 0: the 4-wave register-staged dQ kernel at every head dim
 #endif
+#ifndef ATTN_BWD_DQ_SPLIT
+#define ATTN_BWD_DQ_SPLIT 1 // at d_qk = 192: 1 = the two-group dQ kernel, 0 = the 4-wave one
+#endif
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * kWave;
 constexpr int kDqBlock = kDqWaves * kRows;           // query rows per workgroup
@@ -853,6 +856,195 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   else group_body(GroupTag<false>{});
 }
 
+// ---- dQ with the work split over two wave groups, for d_qk = 192: one wave
+// doing all three products would hold Q, dO, S, dP and six dQ blocks at once,
+// more than the 256 registers of two waves per SIMD.  One workgroup of 8 waves
+// per block of 128 query rows.  Waves 0-3 (dS group) own 32 queries each, keep
+// their Q and dO rows in registers and compute, per 32-key block, S^T = K Q^T,
+// dP^T = V dO^T and dS^T = P (dP - D), which they pass through LDS (bf16,
+// lane for lane); waves 4-7 (dQ group) own the same queries and accumulate
+// dQ^T += K^T dS^T one block later.  Per block each SIMD runs 20 + 12 MFMAs,
+// the 32 of one wave doing all three products, with the other wave's matrix
+// work beside each wave's exponentials.  One barrier per block:
+//   dS group: ... | S, dP, dS(n) -> LDS | S, dP, dS(n+1) -> LDS | ...
+//   dQ group: ... | dQ(n-1)             | dQ(n)                 | ...
+// K tiles (64 keys, stored once in the row layout: the row and the
+// transposing reads are both conflict-free there) and V tiles come by LDS DMA
+// from the dQ group's waves into three buffers.  Tile u+3 is issued in
+// interval 2u+3, once block 2u+1's dQ products (interval 2u+2) have released
+// tile u's buffer, and awaited before interval 2u+5 ends: its first reader
+// runs in interval 2u+6.
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_split_kernel(BwdParams p) {
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
+  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
+  constexpr int TILE_ELEMS = K_ELEMS + V_ELEMS;                        // K rows, V rows
+  constexpr int NBUF = 3;
+  constexpr int DS_ELEMS = kWaves * kWave * 16;                        // 32 x 32 bf16 per dS wave
+  constexpr int DS_HALF = DS_ELEMS / 2 / 8;                            // in 16-byte units
+  constexpr int WORK_ELEMS = NBUF * TILE_ELEMS + 2 * DS_ELEMS;
+  constexpr int STAGE_ELEMS = kWaves * kRows * (DQK + 8);
+  constexpr int LDS_ELEMS = WORK_ELEMS > STAGE_ELEMS ? WORK_ELEMS : STAGE_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
+  constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512, REQ = K_REQ + V_REQ;   // 1 KB requests
+  static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0 && REQ % kWaves == 0, "request split");
+  constexpr int REQ_W = REQ / kWaves;                                  // per dQ-group wave and tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool qgrp = wave >= kWaves;          // dQ group
+  const int wv = wave % kWaves;              // query slice of the wave within its group
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  int h, b, blk;
+  decode_block(p, CAUSAL, h, b, blk);
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int q0 = blk * kBlock;
+  if (q0 >= L) return;                       // uniform over the workgroup
+  const int qw0 = q0 + wv * kRows;
+  const int qrow = qw0 + lq;
+  const bool row_valid = qrow < L;
+  const int kend = CAUSAL ? min(L, q0 + kBlock) : L;
+  const int ntiles = (kend + kTile - 1) / kTile;
+  const int nblk = ntiles * KB;
+  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
+  const Reads<DQK, true> rk(lane);           // K rows and K^T, both from the row layout
+
+  auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t % NBUF) * TILE_ELEMS; };
+  // this lane's 32 bytes of wave wv's dS block, buffer i, as two 16-byte
+  // halves DS_HALF apart (each half of all lanes contiguous: conflict-free)
+  auto dslot = [&] __device__ (int i) __attribute__((always_inline)) {
+    return (lds_u32x4_t*)(lds + NBUF * TILE_ELEMS + i * DS_ELEMS + (wv * kWave + lane) * 8);
+  };
+
+  auto group_body = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
+    constexpr bool QG = decltype(grp_tag)::value;
+    if constexpr (!QG) {
+      bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
+      load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
+      load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
+      const int T = total_tokens(p);
+      const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
+      const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
+      // last key this lane's query sees (-1: none, the row is past the end)
+      const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
+      const Reads<DV> rv(lane);
+      const f32x16_t zero = {};
+      block_sync();                          // the first tiles have landed
+      for (int m = 0; m < nblk; ++m) {
+        const int kb = m % KB;
+        const lds_u16_t* const k_row = buf(m / KB);
+        const lds_u16_t* const v_row = k_row + K_ELEMS;
+        // operands read in groups of at most 6 k-steps beside the resident Q and dO
+        constexpr int CH = QK_STEPS > 8 ? QK_STEPS / 2 : QK_STEPS;
+        f32x16_t s = zero, dp = zero;
+#pragma unroll
+        for (int k0 = 0; k0 < QK_STEPS; k0 += CH) {
+          bf16x8_t a_s[CH];
+#pragma unroll
+          for (int i = 0; i < CH; ++i) a_s[i] = read_row<DQK>(k_row, rk, k0 + i, kb);
+#pragma unroll
+          for (int i = 0; i < CH; ++i) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[i], qreg[k0 + i], s, 0, 0, 0);
+        }
+        bf16x8_t a_p[V_STEPS];
+#pragma unroll
+        for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
+#pragma unroll
+        for (int vs = 0; vs < V_STEPS; ++vs)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
+        const int kb0 = m * 32;                // first key of the block
+        const bool masked = (kb0 + 32 > L) || (qw0 + kRows > L) || (CAUSAL && kb0 + 31 > qw0);
+        // keys visible to this lane's query: up to key_lim (offsets within the block)
+        const int lim = masked ? key_lim - (kb0 + 8 * g) : 64;
+        uint32_t dsb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float d2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * i + e;
+            const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
+            d2[e] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
+          }
+          dsb[i] = pack_bf16x2(d2[0], d2[1]);
+        }
+        lds_u32x4_t* const slot = dslot(m & 1);
+        slot[0] = u32x4_t{dsb[0], dsb[1], dsb[2], dsb[3]};
+        slot[DS_HALF] = u32x4_t{dsb[4], dsb[5], dsb[6], dsb[7]};
+        block_sync();
+      }
+      block_sync();                          // the dQ group's last block
+    } else {
+      const uint32_t k_rowbytes = (uint32_t)(qk_stride * 2), v_rowbytes = (uint32_t)(v_stride * 2);
+      const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK,
+                                                   (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
+      const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV,
+                                                   (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
+      // this wave's requests for tile t: request r = wv * REQ_W + i fills 1 KB
+      // block rr of the K or V copy; lane i writes the 16 bytes at LDS position
+      // 8 i of that block, i.e. chunk `pos` of row `row`, which holds the
+      // tile's chunk pos ^ f(row) of that row.  Rows past the sequence end read
+      // as zeros (the buffer range ends after key L-1).
+      auto issue = [&] __device__ (int t) __attribute__((always_inline)) {
+        lds_u16_t* const base = buf(t);
+#pragma unroll
+        for (int i = 0; i < REQ_W; ++i) {
+          const int r = wv * REQ_W + i;                          // uniform
+          const bool isk = r < K_REQ;
+          const int rr = isk ? r : r - K_REQ;
+          const int D = isk ? DQK : DV;
+          const int e = rr * 512 + 8 * lane;
+          const int row = e / D, pos = (e % D) / 8;
+          const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
+          const uint32_t rowbytes = isk ? k_rowbytes : v_rowbytes;
+          const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
+          attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off, (uint32_t)(t * kTile) * rowbytes,
+                          base + (isk ? 0 : K_ELEMS) + rr * 512);
+        }
+      };
+      f32x16_t acc[QBLK];
+#pragma unroll
+      for (int i = 0; i < QBLK; ++i) acc[i] = f32x16_t{};
+      for (int t = 0; t < NBUF && t < ntiles; ++t) issue(t);
+      attn::dma_wait_all();
+      block_sync();
+      for (int m = 0; m <= nblk; ++m) {
+        const bool refill = (m & 1) && m >= 3 && (m + 3) / 2 < ntiles;
+        if (refill) issue((m + 3) / 2);
+        if (m >= 1) {
+          const int n = m - 1, kb = n % KB;
+          const lds_u16_t* const k_row = buf(n / KB);
+          const lds_u32x4_t* const slot = dslot(n & 1);
+          const u32x4_t praw[2] = {slot[0], slot[DS_HALF]};
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, praw[hh]);
+            bf16x8_t a_q[QBLK];
+#pragma unroll
+            for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_row, rk, db, kb * 32 + 16 * hh);
+#pragma unroll
+            for (int db = 0; db < QBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, acc[db], 0, 0, 0);
+          }
+        }
+        // the tile issued two odd intervals ago has landed before the barrier
+        // ahead of its first reader; this interval's may stay in flight
+        if (m & 1) {
+          if (refill) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(REQ_W) : "memory");
+          else attn::dma_wait_all();
+        }
+        block_sync();
+      }
+      attn::dma_wait_all();
+      store_rows<DQK>(acc, p.scale, lds + wv * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
+    }
+  };
+  if (qgrp) group_body(GroupTag<true>{});
+  else group_body(GroupTag<false>{});
+}
+
 template <int DQK, int DV>
 hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.N * p.H;   // at least T*H; the kernel stops at T*H
@@ -866,8 +1058,13 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
     if (causal) hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
     else hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
   } else {
-    if (causal) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+    if constexpr (ATTN_BWD_DQ_SPLIT && DQK > 128) {
+      if (causal) hipLaunchKernelGGL((bwd_dq_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
+      else hipLaunchKernelGGL((bwd_dq_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
+    } else {
+      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
+    }
   }
   return hipGetLastError();
 }
