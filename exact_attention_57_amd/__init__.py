@@ -170,9 +170,14 @@ def _check_inputs(names_tensors, dtypes, what):
     return first.device
 
 
-def _check_stats(stats, device):
+# uint64 words per workgroup record that the instrumented build (check_build
+# ("stamps")) writes after the four counters of ``stats``
+STAMP_RECORD_WORDS = 16
+
+
+def _check_stats(stats, device, min_numel=4):
     import torch
-    _check_tensor("stats", stats, (torch.int64, torch.uint64), device, min_numel=4)
+    _check_tensor("stats", stats, (torch.int64, torch.uint64), device, min_numel=min_numel)
 
 
 def default_opts() -> FwdOpts:
@@ -257,7 +262,11 @@ def fwd(q, k, v, o=None, lse=None, cu_seqlens=None, *, max_seqlen=None, causal=F
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     _check_tensor("lse", lse, (torch.float32,), dev, shape=(H, T))
     if stats is not None:
-        _check_stats(stats, dev)
+        words = 4
+        if _lib is not None and _lib is _check_libs.get("stamps"):
+            # one record per workgroup of the grid (B * H * query blocks)
+            words += STAMP_RECORD_WORDS * B * H * (-(-N // geometry(d_qk, d_v)["rows_per_item"]))
+        _check_stats(stats, dev, words)
     if scale is None:
         scale = 1.0 / math.sqrt(d_qk)
     if block_mask is not None:

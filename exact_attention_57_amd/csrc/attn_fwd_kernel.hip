@@ -157,6 +157,10 @@ void attn_fwd_kernel(FwdParams p) {
   //   (with the operand prefetch) and the barrier after those, [12..15] the
   //   same for wave 4 (the other group on the same SIMD).
   // The stamps wait for the counter reads, so this build runs a little slower.
+  // It leaves the four counters alone: every wave adding to the same four
+  // words at its end makes the workgroups that finish together (a round of
+  // equal work items) queue on those atomics and leave their CUs late, which
+  // would show up in the records as idle time between workgroups.
 #if ATTN_STAMPS
   const uint64_t rt_start = realtime_now();
   const uint64_t cy_start = cycles_now();
@@ -771,7 +775,7 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 #endif
-  if (p.stats) {
+  if (!ATTN_STAMPS && p.stats) {
     // wave totals -> one atomic per counter per wave
     if (lane == 0) {
       atomicAdd((unsigned long long*)&p.stats[0], (unsigned long long)n_considered);

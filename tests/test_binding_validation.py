@@ -90,6 +90,22 @@ def test_fwd_rejects_bad_buffers(cpu_binding, kw, msg):
         ea.fwd(q, k, v, **kw)
 
 
+def test_fwd_stamps_build_needs_the_record_area(cpu_binding, monkeypatch):
+    # the instrumented build writes one record per workgroup after the four counters
+    fake = _NoCalls()
+    monkeypatch.setitem(ea._check_libs, "stamps", fake)
+    # the library states the rows per workgroup; here 256 stands in for it
+    monkeypatch.setattr(ea, "geometry", lambda d_qk, d_v: {"rows_per_item": 256, "keys_per_tile": 128})
+    q, k, v = _qkv()                       # B=2, N=40, H=3: one query block per (sequence, head)
+    need = 4 + ea.STAMP_RECORD_WORDS * 2 * 3
+    with pytest.raises(ValueError, match=f"stats needs at least {need}"):
+        ea.fwd(q, k, v, max_seqlen=40, stats=torch.zeros(need - 1, dtype=torch.int64), _lib=fake)
+    with pytest.raises(AssertionError, match="reached"):   # a whole record area passes the checks
+        ea.fwd(q, k, v, max_seqlen=40, stats=torch.zeros(need, dtype=torch.int64), _lib=fake)
+    with pytest.raises(AssertionError, match="reached"):   # the default build needs the counters only
+        ea.fwd(q, k, v, max_seqlen=40, stats=torch.zeros(4, dtype=torch.int64))
+
+
 def test_fwd_packed_cu_seqlens_checked(cpu_binding):
     q = torch.zeros(100, 2, 64, dtype=bf16)
     with pytest.raises(ValueError, match="cu_seqlens must have dtype"):

@@ -11,7 +11,8 @@
 * Instrumented build (``libattn_stamps.so``, ATTN_STAMPS): the same outputs bit
   for bit, and its per-workgroup records must be complete and consistent with
   the work decomposition: every (head, sequence, query block) exactly once,
-  tile-loop iterations equal to the closed form, start before end.
+  tile-loop iterations equal to the closed form, start before end; the four
+  counters stay zero (this build keeps only the records).
 """
 import numpy as np
 import pytest
@@ -128,5 +129,4 @@ def test_stamps_build_records(causal, schedule):
     xcc = (rec[:, 2] >> np.uint64(32)).astype(np.int64)
     assert np.all((xcc >= 0) & (xcc < 8))
     say(f"  XCC id = workgroup index mod 8 for {np.mean(xcc == np.arange(W) % 8):.3f} of the workgroups")
-    cnt = buf[:4].cpu().numpy()
-    assert cnt[3] == sum(1 for (h, bb, qb) in items if qb * rows < LENGTHS[bb])
+    assert not buf[:4].any(), "the instrumented build keeps no counters"
