@@ -983,11 +983,25 @@ void bwd_dq_split_kernel(BwdParams p) {
                                                    (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
       const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV,
                                                    (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
-      // this wave's requests for tile t: request r = wv * REQ_W + i fills 1 KB
+      // this wave's requests for a tile: request r = wv * REQ_W + i fills 1 KB
       // block rr of the K or V copy; lane i writes the 16 bytes at LDS position
       // 8 i of that block, i.e. chunk `pos` of row `row`, which holds the
       // tile's chunk pos ^ f(row) of that row.  Rows past the sequence end read
-      // as zeros (the buffer range ends after key L-1).
+      // as zeros (the buffer range ends after key L-1).  The lane offsets are
+      // the same for every tile and are computed once (the row length differs
+      // between K and V, so each costs an integer division).
+      uint32_t lane_off[REQ_W];
+#pragma unroll
+      for (int i = 0; i < REQ_W; ++i) {
+        const int r = wv * REQ_W + i;                            // uniform
+        const bool isk = r < K_REQ;
+        const int rr = isk ? r : r - K_REQ;
+        const int D = isk ? DQK : DV;
+        const int e = rr * 512 + 8 * lane;
+        const int row = e / D, pos = (e % D) / 8;
+        const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
+        lane_off[i] = (uint32_t)row * (isk ? k_rowbytes : v_rowbytes) + (uint32_t)(pos ^ f) * 16u;
+      }
       auto issue = [&] __device__ (int t) __attribute__((always_inline)) {
         lds_u16_t* const base = buf(t);
 #pragma unroll
@@ -995,13 +1009,8 @@ void bwd_dq_split_kernel(BwdParams p) {
           const int r = wv * REQ_W + i;                          // uniform
           const bool isk = r < K_REQ;
           const int rr = isk ? r : r - K_REQ;
-          const int D = isk ? DQK : DV;
-          const int e = rr * 512 + 8 * lane;
-          const int row = e / D, pos = (e % D) / 8;
-          const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
           const uint32_t rowbytes = isk ? k_rowbytes : v_rowbytes;
-          const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
-          attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off, (uint32_t)(t * kTile) * rowbytes,
+          attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off[i], (uint32_t)(t * kTile) * rowbytes,
                           base + (isk ? 0 : K_ELEMS) + rr * 512);
         }
       };
