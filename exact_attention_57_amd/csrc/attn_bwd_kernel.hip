@@ -45,7 +45,7 @@
 #include "attn_fwd_common.h"   // LDS DMA requests, buffer resources, barriers (namespace attn)
 
 #ifndef ATTN_BWD_PREFETCH
-#define ATTN_BWD_PREFETCH 1  // dK/dV at d <= 128: a block's transposed operands read a phase early
+#define ATTN_BWD_PREFETCH 1  // dK/dV: a block's transposed operands read a phase early (d_qk = 192: dV group only)
 #endif
 
 namespace attn_grad {
@@ -697,7 +697,9 @@ void bwd_dkdv_split_kernel(BwdParams p) {
     // products, read at the end of half_a: that block's rows are visible from
     // the barrier before half_a on (half_a reads them too), and a half_b that
     // starts with its operands in registers does not wait for LDS first.
-    constexpr bool PRE = !Q_ONCE && ATTN_BWD_PREFETCH;
+    // At d_qk = 192 only the dV group has the registers for it (the dK group
+    // would need 48 more beside its six dK blocks).
+    constexpr bool PRE = (!Q_ONCE || !KG) && ATTN_BWD_PREFETCH;
     bf16x8_t pre[PRE ? 2 : 1][PRE ? ABLK : 1];
     auto prefetch = [&] __device__ (int nb) __attribute__((always_inline)) {
       if constexpr (PRE) {
