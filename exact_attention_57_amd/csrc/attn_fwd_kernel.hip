@@ -24,9 +24,10 @@
 // phase behind group 0, so on every SIMD one wave feeds the matrix core while
 // the other computes exponentials.
 //
-// LDS: two K and two V tile buffers (dense rows, XOR-swizzled 16-byte chunks),
-// filled straight from HBM by buffer_load ... lds at the start of each even
-// phase for the tiles needed two phases later.
+// LDS: three K and two V tile buffers (dense rows, XOR-swizzled 16-byte
+// chunks), filled straight from L2/HBM by buffer_load ... lds requests that
+// group 0 spreads over its matrix phase (V of tile j and K of tile j+2 in
+// iteration j).
 //
 // Method sources (web pages on FlashAttention-4):
 //  * tiling + online softmax with running max/sum: ainexis.cn deep dive,
