@@ -77,12 +77,15 @@ int block_rows() { return kBlock; }
 // LDS layouts of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
 // bytes): chunk c of row r sits at position c ^ f(r).
 //  * row layout, read 16 bytes per lane with 16 consecutive rows per
-//    quarter-wave: f(r) = r mod 16 (R = 16); for R = 8 or 24 a row starts on
-//    alternate halves of the 64 banks, so the 4-bank group of chunk c of row r
-//    is (c ^ f(r) ^ 8 (r mod 2)) mod 16, and f(r) = 4 b1(r) + (r/4) mod 4 (bits
-//    of r/2 rotated) gives the 16 rows of a quarter-wave distinct groups and,
-//    since bit 2 of f follows b1(r), the 4 rows x 4 chunks of a transposing read
-//    from this layout (at (192, 128) the Q tile is stored only in it) too;
+//    quarter-wave, and by ds_read_b64_tr_b16 (4 rows x 4 consecutive chunks
+//    per half-wave, rows r0..r0+3 with r0 a multiple of 4): for R = 16 every
+//    row starts at bank 0, and f(r) = 4 (r mod 4) + (r/4) mod 4 (the two
+//    2-bit halves of r mod 16 swapped) is a permutation of the 16 rows of a
+//    quarter-wave, while its upper two bits, r mod 4, tell the 4 rows of a
+//    transposing read apart; for R = 8 or 24 a row starts on alternate halves
+//    of the 64 banks, so the 4-bank group of chunk c of row r is
+//    (c ^ f(r) ^ 8 (r mod 2)) mod 16, and f(r) = 4 b1(r) + (r/4) mod 4 (bits of
+//    r/2 rotated) does the same.  Tiles read both ways are stored once;
 //  * transposed layout, read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
 //    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8 or 24).
 // Both are invariant under a shift of r by a multiple of 16, and keep a chunk
@@ -90,7 +93,9 @@ int block_rows() { return kBlock; }
 template <int D>
 struct RowSwz {
   static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
-  __device__ static int f(int r) { return (D == 128) ? (r & 15) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)); }
+  __device__ static int f(int r) {
+    return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
 };
 template <int D>
 struct TrSwz {
@@ -405,8 +410,8 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---- dQ with LDS DMA tiles (d_qk = d_v <= 128): one workgroup of 8 waves
 // (two per SIMD) per block of 256 query rows, so each K/V tile fetched from
-// L2 serves twice the rows of the 4-wave kernel above.  The tiles (K in the
-// row and the transposed layout, V in the row layout) are copied HBM/L2 ->
+// L2 serves twice the rows of the 4-wave kernel above.  The tiles (K and V in
+// the row layout; K is also read transposed from it) are copied HBM/L2 ->
 // LDS by buffer_load ... lds, double-buffered: at the start of tile t every
 // wave issues its share of tile t+1's requests into the other buffer (last
 // read in tile t-1, before the barrier that ended it), computes tile t, then
@@ -431,12 +436,12 @@ void bwd_dq_dma_kernel(BwdParams p) {
   static_assert(DQK == DV && DQK <= 128, "DMA dQ kernel: d_qk = d_v = 64 or 128");
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
   constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
-  constexpr int STAGE = 2 * K_ELEMS + V_ELEMS;        // K rows, K transposed, V rows
+  constexpr int STAGE = K_ELEMS + V_ELEMS;            // K rows (also read transposed), V rows
   constexpr int OUT_ELEMS = kDqWaves * kRows * (DQK + 8);
   constexpr int LDS_ELEMS = (2 * STAGE > OUT_ELEMS) ? 2 * STAGE : OUT_ELEMS;
   static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
   constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512;   // 1 KB requests per copy
-  constexpr int REQ = 2 * K_REQ + V_REQ;
+  constexpr int REQ = K_REQ + V_REQ;
   static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0 && REQ % kDqWaves == 0, "request split");
   constexpr int REQ_W = REQ / kDqWaves;                // requests per wave per tile
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
@@ -464,7 +469,7 @@ void bwd_dq_dma_kernel(BwdParams p) {
   const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
   const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
 
-  const Reads<DQK> rk(lane);
+  const Reads<DQK, true> rk(lane);
   const Reads<DV> rv(lane);
   const int kend = CAUSAL ? min(L, q0 + kDqBlock) : L;
   const int ntiles = (kend + kTile - 1) / kTile;
@@ -485,17 +490,16 @@ void bwd_dq_dma_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < REQ_W; ++i) {
       const int r = wave * REQ_W + i;                  // uniform
-      const int copy = r < K_REQ ? 0 : (r < 2 * K_REQ ? 1 : 2);
-      const int rr = r - copy * K_REQ;
-      const int D = copy < 2 ? DQK : DV;
+      const bool isk = r < K_REQ;
+      const int rr = isk ? r : r - K_REQ;
+      const int D = isk ? DQK : DV;
       const int e = rr * 512 + 8 * lane;               // element of the tile (row-major, D per row)
       const int row = e / D, pos = (e % D) / 8;
-      const int f = copy == 0 ? RowSwz<DQK>::f(row) : (copy == 1 ? TrSwz<DQK>::f(row) : RowSwz<DV>::f(row));
-      const uint32_t rowbytes = copy < 2 ? k_rowbytes : v_rowbytes;
+      const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
+      const uint32_t rowbytes = isk ? k_rowbytes : v_rowbytes;
       const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
       const uint32_t tile_off = (uint32_t)(t * kTile) * rowbytes;
-      attn::dma_chunk(copy < 2 ? k_rsrc : v_rsrc, lane_off, tile_off,
-                      base + (copy == 0 ? 0 : (copy == 1 ? K_ELEMS : 2 * K_ELEMS)) + rr * 512);
+      attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off, tile_off, base + (isk ? 0 : K_ELEMS) + rr * 512);
     }
   };
 
@@ -509,8 +513,7 @@ void bwd_dq_dma_kernel(BwdParams p) {
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
     const lds_u16_t* const k_row = stage(t & 1);
-    const lds_u16_t* const k_tr = k_row + K_ELEMS;
-    const lds_u16_t* const v_row = k_row + 2 * K_ELEMS;
+    const lds_u16_t* const v_row = k_row + K_ELEMS;
     const int k0 = t * kTile;
     const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
 #pragma unroll
@@ -543,7 +546,7 @@ void bwd_dq_dma_kernel(BwdParams p) {
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
         bf16x8_t a_q[QBLK];
 #pragma unroll
-        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
+        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_row, rk, db, kb * 32 + 16 * hh);
 #pragma unroll
         for (int db = 0; db < QBLK; ++db)
           dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
@@ -573,13 +576,12 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)
 void bwd_dkdv_split_kernel(BwdParams p) {
   constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, KBLK = DQK / 32, VBLK = DV / 32, QB = kTile / 32;
   constexpr int Q_ELEMS = kTile * DQK, O_ELEMS = kTile * DV;
-  // Q is read row-wise (S) and transposed (dK); at d_qk = 192 two copies of
-  // two buffers would not fit in LDS, so the tile is stored once, in the row
-  // layout, which serves both reads without bank conflicts
-  constexpr bool Q_ONCE = DQK > 128;
-  constexpr int QS = (Q_ONCE ? 1 : 2) * Q_ELEMS;                       // Q elements stored per tile
-  // + LSE (log2 units) and D as fp32, padded to whole 1 KB blocks
-  constexpr int TILE_ELEMS = (QS + 2 * O_ELEMS + 2 * kTile * 2 + 511) / 512 * 512;
+  // Q is read row-wise (S) and transposed (dK), dO row-wise (dP) and
+  // transposed (dV): each tile is stored once, in the row layout, which
+  // serves both reads without bank conflicts.  Per buffer: Q, dO, then LSE
+  // (log2 units) and D as fp32, padded to whole 1 KB blocks.
+  constexpr int ROWS_OFF = Q_ELEMS + O_ELEMS;                           // LSE, D rows
+  constexpr int TILE_ELEMS = (ROWS_OFF + 2 * kTile * 2 + 511) / 512 * 512;
   constexpr int P_ELEMS = kWaves * kWave * 16;                          // 32 x 32 bf16 per dV wave
   constexpr int STAGE_ELEMS = 2 * kWaves * kRows * ((DQK > DV ? DQK : DV) + 8);
   constexpr int WORK_ELEMS = 2 * TILE_ELEMS + 2 * P_ELEMS;
@@ -604,8 +606,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   const bool key_valid = key < L;
 
 
-  const Reads<DQK, Q_ONCE> rq(lane);
-  const Reads<DV> ro(lane);
+  const Reads<DQK, true> rq(lane);
+  const Reads<DV, true> ro(lane);
   const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
   const int ntiles = (L - qstart + kTile - 1) / kTile;
   const int nblk = ntiles * QB;
@@ -620,15 +622,12 @@ void bwd_dkdv_split_kernel(BwdParams p) {
 
   auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t & 1) * TILE_ELEMS; };
   // Q and dO tiles are copied HBM/L2 -> LDS by buffer_load ... lds, every wave
-  // issuing its share of the tile's 1 KB requests: the Q rows in the row
-  // layout (and, up to d_qk = 128, again in the transposed layout) and the dO
-  // rows in both layouts.  Request lane i writes the 16 bytes at LDS position
-  // 8 i of its block, i.e. chunk `pos` of row `row`, which holds the tile's
-  // chunk pos ^ f(row) of that row.  The buffer ranges end after row L-1 of
-  // the sequence, so rows past its end read as zeros.
-  constexpr int Q_REQ = Q_ELEMS / 512, O_REQ = O_ELEMS / 512;   // 1 KB requests per copy
-  constexpr int NQCOPY = Q_ONCE ? 1 : 2;
-  constexpr int REQ = NQCOPY * Q_REQ + 2 * O_REQ;
+  // issuing its share of the tile's 1 KB requests.  Request lane i writes the
+  // 16 bytes at LDS position 8 i of its block, i.e. chunk `pos` of row `row`,
+  // which holds the tile's chunk pos ^ f(row) of that row.  The buffer ranges
+  // end after row L-1 of the sequence, so rows past its end read as zeros.
+  constexpr int Q_REQ = Q_ELEMS / 512, O_REQ = O_ELEMS / 512;   // 1 KB requests per tile
+  constexpr int REQ = Q_REQ + O_REQ;
   static_assert(Q_ELEMS % 512 == 0 && O_ELEMS % 512 == 0 && REQ % (2 * kWaves) == 0, "request split");
   constexpr int REQ_W = REQ / (2 * kWaves);                      // requests per wave per tile
   const uint32_t q_rowbytes = (uint32_t)(qk_stride * 2), o_rowbytes = (uint32_t)(v_stride * 2);
@@ -640,18 +639,15 @@ void bwd_dkdv_split_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < REQ_W; ++i) {
       const int r = wave * REQ_W + i;                            // uniform
-      const bool isq = r < NQCOPY * Q_REQ;
-      const int copy = isq ? r / Q_REQ : 2 + (r - NQCOPY * Q_REQ) / O_REQ;   // 0, 1: Q row, tr; 2, 3: dO row, tr
-      const int rr = isq ? r % Q_REQ : (r - NQCOPY * Q_REQ) % O_REQ;
+      const bool isq = r < Q_REQ;
+      const int rr = isq ? r : r - Q_REQ;
       const int D = isq ? DQK : DV;
-      const int e = rr * 512 + 8 * lane;                         // element of the copy (row-major, D per row)
+      const int e = rr * 512 + 8 * lane;                         // element of the tile (row-major, D per row)
       const int row = e / D, pos = (e % D) / 8;
-      const int f = copy == 0 ? RowSwz<DQK>::f(row)
-                  : copy == 1 ? TrSwz<DQK>::f(row)
-                  : copy == 2 ? RowSwz<DV>::f(row) : TrSwz<DV>::f(row);
+      const int f = isq ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
       const uint32_t rowbytes = isq ? q_rowbytes : o_rowbytes;
       const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
-      lds_u16_t* const dst = base + (copy == 0 ? 0 : copy == 1 ? Q_ELEMS : copy == 2 ? QS : QS + O_ELEMS) + rr * 512;
+      lds_u16_t* const dst = base + (isq ? 0 : Q_ELEMS) + rr * 512;
       attn::dma_chunk(isq ? q_rsrc : o_rsrc, lane_off, q0t * rowbytes, dst);
     }
   };
@@ -665,7 +661,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
     if (tid < 2 * kTile) rowval = (r < L) ? (tid < kTile ? lse_h[r] : d_h[r]) : 0.0f;
   };
   auto stage_rows = [&] __device__ (int t) __attribute__((always_inline)) {
-    if (tid < 2 * kTile) ((lds_f32_t*)(buf(t) + QS + 2 * O_ELEMS))[tid] = tid < kTile ? rowval * kLog2e : rowval;
+    if (tid < 2 * kTile) ((lds_f32_t*)(buf(t) + ROWS_OFF))[tid] = tid < kTile ? rowval * kLog2e : rowval;
   };
   // this lane's 32 bytes of the P block of key slice wv, buffer i, as two
   // 16-byte halves P_HALF apart: each half of all lanes is contiguous, so the
@@ -699,7 +695,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
     // starts with its operands in registers does not wait for LDS first.
     // At d_qk = 192 only the dV group has the registers for it (the dK group
     // would need 48 more beside its six dK blocks).
-    constexpr bool PRE = (!Q_ONCE || !KG) && ATTN_BWD_PREFETCH;
+    constexpr bool PRE = (DQK <= 128 || !KG) && ATTN_BWD_PREFETCH;
     bf16x8_t pre[PRE ? 2 : 1][PRE ? ABLK : 1];
     auto prefetch = [&] __device__ (int nb) __attribute__((always_inline)) {
       if constexpr (PRE) {
@@ -709,8 +705,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
         for (int hh = 0; hh < 2; ++hh)
   #pragma unroll
           for (int db = 0; db < ABLK; ++db)
-            pre[hh][db] = KG ? read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh)
-                             : read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+            pre[hh][db] = KG ? read_tr<DQK>(base, rq, db, qb * 32 + 16 * hh)
+                             : read_tr<DV>(base + Q_ELEMS, ro, db, qb * 32 + 16 * hh);
       }
     };
     // first half of block nb: dV group S, P -> LDS; dK group dP
@@ -730,7 +726,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   #pragma unroll
           for (int i = 0; i < CH; ++i) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[i], breg[k0 + i], s, 0, 0, 0);
         }
-        const lds_f32_t* const lse_s = (const lds_f32_t*)(base + QS + 2 * O_ELEMS);
+        const lds_f32_t* const lse_s = (const lds_f32_t*)(base + ROWS_OFF);
         const int q0t = qstart + t * kTile;
         const bool masked = (q0t + kTile > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q0t);
         float x[16];
@@ -758,7 +754,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
       } else {
         bf16x8_t a_p[V_STEPS];
   #pragma unroll
-        for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + QS, ro, vs, qb);
+        for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(base + Q_ELEMS, ro, vs, qb);
         carry = zero;
   #pragma unroll
         for (int vs = 0; vs < V_STEPS; ++vs)
@@ -779,12 +775,12 @@ void bwd_dkdv_split_kernel(BwdParams p) {
           bf16x8_t a_v[VBLK];
   #pragma unroll
           for (int db = 0; db < VBLK; ++db)
-            a_v[db] = PRE ? pre[PRE ? hh : 0][PRE ? db : 0] : read_tr<DV>(base + QS + O_ELEMS, ro, db, qb * 32 + 16 * hh);
+            a_v[db] = PRE ? pre[PRE ? hh : 0][PRE ? db : 0] : read_tr<DV>(base + Q_ELEMS, ro, db, qb * 32 + 16 * hh);
   #pragma unroll
           for (int db = 0; db < VBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_v[db], bop, acc[db], 0, 0, 0);
         }
       } else {
-        const lds_f32_t* const d_s = (const lds_f32_t*)(base + QS + 2 * O_ELEMS) + kTile;
+        const lds_f32_t* const d_s = (const lds_f32_t*)(base + ROWS_OFF) + kTile;
         const lds_u32x4_t* const slot = pslot(nb & 1);
         const u32x4_t praw[2] = {slot[0], slot[P_HALF]};
   #pragma unroll
@@ -802,7 +798,7 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   #pragma unroll
           for (int db = 0; db < KBLK; ++db)
             a_k[db] = PRE ? pre[PRE ? hh : 0][PRE ? db : 0]
-                          : read_tr<DQK>(base + (Q_ONCE ? 0 : Q_ELEMS), rq, db, qb * 32 + 16 * hh);
+                          : read_tr<DQK>(base, rq, db, qb * 32 + 16 * hh);
   #pragma unroll
           for (int db = 0; db < KBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k[db], bop, acc[db], 0, 0, 0);
         }
