@@ -323,8 +323,9 @@ def _cpu_model() -> str:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # the chip takes about 50 launches of this kernel to reach its steady clock
-    # (the first 50 run ~14 % slower); 100 untimed warm-up launches skip that ramp
+    # in a fresh process the chip's clock dips to ~1.3 GHz around launches 5-10
+    # of this kernel and recovers after ~30 (--ramp shows it); 100 untimed
+    # warm-up launches get past the dip
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
@@ -347,6 +348,10 @@ def main():
                     help="time the instrumented build (libattn_stamps.so) of the bf16 forward pass and summarise "
                          "its per-workgroup records: dispatch order, XCD mapping, per-CU balance, finish tail, "
                          "cycles per phase")
+    ap.add_argument("--ramp", type=int, default=0, metavar="N",
+                    help="only time the first N launches of the bf16 forward pass in this process one by one "
+                         "(instrumented build, no warm-up) and report, for some of them, the shader clock and the "
+                         "cycles per workgroup from the per-workgroup records")
     ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
                     help="only time the vendor library's bf16 GEMM (torch.matmul, N x N x N, fp32 accumulation) "
                          "with --warmup and --steps launches, as a practical matrix-core ceiling on this chip")
@@ -438,6 +443,41 @@ def main():
                scale=inp["scale"], rescale_threshold_log2=args.tau,
                poly_exp_sixteenths=args.poly, schedule=args.schedule, block_mask=bmask_dev, stream=stream,
                _lib=fwd_lib)
+
+    if args.ramp:
+        if args.bwd or args.fp8 or args.block_density is not None:
+            raise SystemExit("--ramp follows the dense bf16 forward pass")
+        st_lib = ea.check_build("stamps")
+        geo = ea.geometry(wl.d_qk, wl.d_v)
+        W = inp["B"] * H * (-(-inp["N"] // geo["rows_per_item"]))
+        n = args.ramp
+        rec_at = [i for i in (1, 2, 3, 4, 5, 6, 8, 10, 15, 20, 25, 30, 40, 60, 80, 120, 160, 200, 300, 400) if i <= n]
+        bufs = {i: torch.zeros(4 + STAMP_WORDS * W, dtype=torch.int64, device="cuda") for i in rec_at}
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(1, n + 1):
+            ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
+                   scale=inp["scale"], rescale_threshold_log2=args.tau, poly_exp_sixteenths=args.poly,
+                   schedule=args.schedule, stats=bufs.get(i), stream=stream, _lib=st_lib)
+            evs[i].record(stream)
+        torch.cuda.synchronize()
+        ms = [evs[i - 1].elapsed_time(evs[i]) for i in range(1, n + 1)]
+        recs = {}
+        for i in rec_at:
+            r = bufs[i][4:].cpu().numpy().view(np.uint64).reshape(W, STAMP_WORDS).astype(np.float64)
+            ran = r[:, 4] > 0
+            cyc = r[ran, 5] + r[ran, 6] + r[ran, 7]
+            dur = (r[ran, 1] - r[ran, 0]) / REALTIME_HZ
+            recs[str(i)] = {"ms": round(ms[i - 1], 4), "cycles_per_workgroup": int(np.median(cyc)),
+                            "shader_clock_ghz": round(float(np.median(cyc / dur)) / 1e9, 3)}
+        win = ms[5:25]                            # the launches a run with 5 warm-ups and 20 timed steps times
+        print(json.dumps({"ramp": wl.key, "launches": n, "ms_per_launch": [round(x, 4) for x in ms],
+                          "recorded": recs,
+                          "mean_ms_launches_6_to_25": round(sum(win) / len(win), 4) if len(win) == 20 else None,
+                          "mean_ms_last_20": round(sum(ms[-20:]) / 20, 4) if n >= 20 else None,
+                          "flop_per_launch": flops}), flush=True)
+        return
 
     f8 = None
     if args.fp8:
