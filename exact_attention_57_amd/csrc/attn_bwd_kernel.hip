@@ -23,10 +23,13 @@
 // Layout of the work on the chip: each wave owns 32 rows of its workgroup's
 // block; a 64-row tile of the streamed operands (Q and dO for dK/dV, K and V
 // for dQ) is staged in LDS once per workgroup and read by all its waves.
-// Both kernels keep every wave within 256 registers so that each SIMD runs
-// two waves: the dQ kernel as two 4-wave workgroups per CU, the dK/dV kernel
-// as one 8-wave workgroup whose two halves split the products between them.  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators:
+// Every kernel keeps each wave within 256 registers so that each SIMD runs
+// two waves: the dK/dV kernel as one 8-wave workgroup whose two halves split
+// the products between them; the dQ kernel, up to d_qk = 128, as one 8-wave
+// workgroup of 256 queries whose waves each do all three products, and at
+// d_qk = 192 as one 8-wave workgroup of 128 queries split like the dK/dV
+// kernel (a 4-wave register-staged dQ kernel remains as a build option).  The
+// matrix products are v_mfma_f32_32x32x16_bf16 with fp32 accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
 //   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V in registers)
@@ -36,8 +39,9 @@
 // row index swapped, accumulator registers 0..7 and 8..15 of a 32 x 32
 // block hold 8 consecutive rows -- the B-operand slots of the next product --
 // so P and dS go from the accumulators to bf16 B operands in registers.  A
-// tile read both row-wise and transposed is stored twice, once in each
-// swizzled layout, so both reads are free of bank conflicts.
+// tile read both row-wise and transposed is stored once, in a row layout whose
+// swizzle keeps both kinds of read free of bank conflicts (RowSwz below), and
+// the streamed tiles are copied HBM/L2 -> LDS by buffer_load ... lds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,10 +90,12 @@ int block_rows() { return kBlock; }
 //    of the 64 banks, so the 4-bank group of chunk c of row r is
 //    (c ^ f(r) ^ 8 (r mod 2)) mod 16, and f(r) = 4 b1(r) + (r/4) mod 4 (bits of
 //    r/2 rotated) does the same.  Tiles read both ways are stored once;
-//  * transposed layout, read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
+//  * transposed layout (only the 4-wave register-staged dQ kernel keeps a
+//    second copy in it), read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
 //    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8 or 24).
-// Both are invariant under a shift of r by a multiple of 16, and keep a chunk
-// inside its aligned group of 8, so c ^ f(r) < R.
+// Both are invariant under a shift of r by a multiple of 16 and keep
+// c ^ f(r) < R: for R = 16 both are 4-bit values, for R = 8 and 24 f < 8
+// keeps a chunk inside its aligned group of 8.
 template <int D>
 struct RowSwz {
   static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
