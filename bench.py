@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
                     [--tau 8.0] [--poly 0] [--schedule 0|1] [--no-cpu-baseline]
                     [--bwd] [--block-density D] [--fp8] [--stamps] [--stats]
+    python bench.py --ramp N | --gemm-ceiling N | --copy-calibration MIB
 
 A step is one call of attn_fwd over the whole workload (all query blocks of
 all heads and sequences).  Default workload: non-causal B=4 H=16 N=4096
@@ -43,12 +44,20 @@ MFMA peak (5.0 PFLOP/s), with the percentage of the bf16 peak alongside.
 
 --stamps times the instrumented build of the bf16 forward pass
 (libattn_stamps.so: the same kernels plus per-workgroup clock stamps), then
-runs it once more with a record buffer and adds a "stamps" summary: the
-XCD each workgroup ran on against its grid index, per-XCD and per-CU busy
-time, the finish-time tail (last workgroup end minus the median end), the
+runs it ~50 ms more with a record buffer and adds a "stamps" summary of the
+last launch: the XCD each workgroup ran on against its grid index, per-XCD
+and per-CU busy time and last finish, workgroups per CU and the gaps between
+them, the finish-time tail (last workgroup end minus the median end), the
 start order against the grid index and against the work per item, and the
 shader cycles per tile iteration of each phase (matrix, barrier, softmax,
 barrier) for one wave of each ping-pong group.
+
+--ramp N only times the first N launches of the instrumented bf16 forward in
+this process one by one, and reads the shader clock and cycles per workgroup
+of selected launches from their records (the clock dip of the first launches).
+--gemm-ceiling N only times the vendor bf16 GEMM (torch.matmul, N^3);
+--copy-calibration MIB only runs a plain copy kernel over MIB MiB, for scaling
+the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
