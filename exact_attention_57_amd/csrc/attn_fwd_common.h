@@ -61,7 +61,8 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kRowsPerWave * kWaves;   // query rows per workgroup
 // Keys per tile: 128 where the registers allow it (d_qk <= 128), else 64
-// (96 also fits at d_qk = 192 but measured slower).
+// (96 also fits at d_qk = 192 but measured no faster, and the block-sparse
+// kernel needs tiles that divide its 128-key mask blocks).
 // Larger tiles halve the per-tile cost of the phase barriers and the
 // softmax's row-wide steps.
 #ifndef ATTN_BLOCK_N_SMALL_D
