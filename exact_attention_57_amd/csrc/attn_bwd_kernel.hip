@@ -26,9 +26,10 @@
 // Every kernel keeps each wave within 256 registers so that each SIMD runs
 // two waves: the dK/dV kernel as one 8-wave workgroup whose two halves split
 // the products between them; the dQ kernel, up to d_qk = 128, as one 8-wave
-// workgroup of 256 queries whose waves each do all three products, and at
-// d_qk = 192 as one 8-wave workgroup of 128 queries split like the dK/dV
-// kernel (a 4-wave register-staged dQ kernel remains as a build option).  The
+// workgroup of 256 queries whose waves each do all three products, in two
+// groups that alternate matrix and VALU phases as the forward kernel does, and
+// at d_qk = 192 as one 8-wave workgroup of 128 queries split like the dK/dV
+// kernel (earlier dQ kernels remain as build options).  The
 // matrix products are v_mfma_f32_32x32x16_bf16 with fp32 accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
@@ -423,7 +424,8 @@ void bwd_dq_kernel(BwdParams p) {
 // read in tile t-1, before the barrier that ended it), computes tile t, then
 // waits for its requests and meets the others at the barrier, after which
 // tile t+1 is complete.  Rows past the sequence end read as zeros (the buffer
-// range ends after key L-1).  Per-wave arithmetic as in bwd_dq_kernel.
+// range ends after key L-1).  Per-wave arithmetic as in bwd_dq_kernel.  The
+// ping-pong kernel below replaces it by default (ATTN_BWD_DQ_PP).
 #ifndef ATTN_BWD_DQ_DMA
 #define ATTN_BWD_DQ_DMA 1   // 0: the 4-wave register-staged dQ kernel at every head dim
 #endif
@@ -560,6 +562,262 @@ void bwd_dq_dma_kernel(BwdParams p) {
     }
     attn::dma_wait_barrier<0>();                       // tile t+1 has landed; stage t & 1 is free
   }
+  store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
+}
+
+// ---- dQ in two ping-pong wave groups (d_qk = d_v <= 128): the forward
+// kernel's schedule applied to the dQ pass.  One workgroup of 8 waves per
+// block of 256 query rows; each wave owns 32 rows (Q and dO as B operands,
+// LSE and D in registers) and runs, per 64-key tile j, a matrix phase -- one
+// stream of MFMAs: dQ^T += K_{j-1}^T dS_{j-1}^T, S^T_j = K_j Q^T,
+// dP^T_j = V_j dO^T -- and a VALU phase: P_j = 2^(c S_j - LSE log2 e) and
+// dS_j = P_j (dP_j - D) as bf16 B operands of the next matrix phase.  Waves
+// 0-3 (group 0) and 4-7 (group 1) put one wave of each group on every SIMD
+// and run half an iteration apart, separated by workgroup barriers, so that
+// one group's MFMAs overlap the other group's VALU work:
+//   group 0: | matrix(j)  | VALU(j)   | matrix(j+1) | ...
+//   group 1: | VALU(j-1)  | matrix(j) | VALU(j)     | ...
+// K tile t lives in K buffer t mod 3 and V tile t in V buffer t mod 2; group
+// 0 spreads the DMAs of tile j+1 over its matrix phase j and waits for them
+// before the barrier that ends iteration j.  The buffers they fill were last
+// read in iteration j-1 (K_{j-2} by the dQ product of matrix(j-1), V_{j-1} by
+// its dP product).  Matrix(0)'s dQ product multiplies zero dS with the
+// zero-filled K buffer 2, and matrix(ntiles)'s score and dP products read a
+// tile past the sequence end (zeros) and are dropped, so every iteration runs
+// the same code.  The dQ slots come first in the stream: their operands
+// (K_{j-1}, resident since iteration j-2) are read at the end of the wave's
+// previous phase, before the tile DMAs of the current one have landed.
+#ifndef ATTN_BWD_DQ_PP
+#define ATTN_BWD_DQ_PP 1    // 1: the ping-pong dQ kernel at d_qk = d_v <= 128, 0: the 8-wave DMA-fed one
+#endif
+constexpr int kPpPrefetch = 4;                        // matrix-phase LDS operands read this many slots ahead
+
+// Per slot of the matrix phase: LDS reads issued ahead (two transposing reads
+// for a dQ slot, one 16-byte read otherwise), then the MFMA.
+template <int S, int NS, int NDQ>
+__device__ __forceinline__ void pin_dq_schedule() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  if constexpr (S < NS) {
+    if constexpr (S + kPpPrefetch < NS)
+      __builtin_amdgcn_sched_group_barrier(kDsRead, (S + kPpPrefetch < NDQ) ? 2 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    pin_dq_schedule<S + 1, NS, NDQ>();
+  }
+}
+
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_pp_kernel(BwdParams p) {
+  static_assert(DQK == DV && DQK <= 128, "ping-pong dQ kernel: d_qk = d_v = 64 or 128");
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
+  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
+  constexpr int kKBufs = 3, kVBufs = 2;
+  constexpr int TILE_LDS = kKBufs * K_ELEMS + kVBufs * V_ELEMS;
+  constexpr int OUT_ELEMS = kDqWaves * kRows * (DQK + 8);
+  constexpr int LDS_ELEMS = TILE_LDS > OUT_ELEMS ? TILE_LDS : OUT_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
+  constexpr int kLoaders = kDqWaves / 2;              // group 0 issues the tile DMAs
+  constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512;   // 1 KB requests per tile
+  static_assert(K_REQ % kLoaders == 0 && V_REQ % kLoaders == 0, "request split");
+  constexpr int K_ISS = K_REQ / kLoaders, V_ISS = V_REQ / kLoaders, ISS = K_ISS + V_ISS;
+  // A 1 KB request covers 512 / D rows; the swizzle of a row depends on its
+  // index mod 16, so a request's lane offsets repeat every D / 32 requests,
+  // and a loader's K_ISS = D / 32 requests per copy need D / 32 of them.
+  constexpr int ROWS_REQ = 512 / DQK, PERIOD = DQK / 32;
+  static_assert(K_ISS == PERIOD && V_ISS == PERIOD, "one lane offset per request of a copy");
+  // matrix-phase slots: dQ (kb, hh, db), then score (ks, kb), then dP (vs, kb)
+  constexpr int NDQ = KB * 2 * QBLK, NQK = QK_STEPS * KB, NDP = V_STEPS * KB;
+  constexpr int NS = NDQ + NQK + NDP;
+  static_assert(kPpPrefetch <= NDQ, "prefetched slots are dQ slots");
+  constexpr int kDmaStride = NS / ISS;
+  static_assert(kDmaStride >= 1, "DMAs per matrix phase");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+  auto kbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * K_ELEMS; };
+  auto vbuf = [&] __device__ (int i) __attribute__((always_inline)) { return lds + kKBufs * K_ELEMS + i * V_ELEMS; };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave / kLoaders, lw = wave % kLoaders;
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  const int nblk = (p.N + kDqBlock - 1) / kDqBlock;
+  int h, b, blk;
+  decode_block_n(p, nblk, CAUSAL, h, b, blk);
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int q0 = blk * kDqBlock;
+  if (q0 >= L) return;                                 // uniform over the workgroup
+  const int qw0 = q0 + wave * kRows;
+  const int qrow = qw0 + lq;
+  const bool row_valid = qrow < L;
+
+  bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
+  load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
+  load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
+  const int T = total_tokens(p);
+  const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
+  const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
+  const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
+  const float c = p.c;
+
+  const Reads<DQK, true> rk(lane);                     // K rows and K^T; V rows (d_v = d_qk) alike
+  const int kend = CAUSAL ? min(L, q0 + kDqBlock) : L;
+  const int ntiles = (kend + kTile - 1) / kTile;
+  const int64_t row_elems = (int64_t)p.H * DQK;        // = H * d_v
+  const uint32_t rowbytes = (uint32_t)(row_elems * 2);
+  const uint32_t seq_bytes = (uint32_t)((L - 1) * row_elems * 2 + DQK * 2);
+  const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * row_elems + (int64_t)h * DQK, seq_bytes);
+  const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * row_elems + (int64_t)h * DV, seq_bytes);
+  // byte offset of tile t; a tile past the last one starts at the resources'
+  // end, so its DMAs return zeros without touching memory
+  auto tile_off = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * kTile) * rowbytes : seq_bytes;
+  };
+  // Lane offsets of a copy's request rr = lw * PERIOD + i (its rows from
+  // rr * ROWS_REQ on; the row offset goes into the uniform soffset): lane l
+  // writes the 16 bytes at LDS position 8 l of the request's 1 KB block, i.e.
+  // chunk `pos` of row rr * ROWS_REQ + r, which holds the tile's chunk
+  // pos ^ f(row) of that row.  f depends on the row mod 16, and
+  // PERIOD * ROWS_REQ = 16, so it depends on i, not on lw.
+  uint32_t lane_off[PERIOD];
+#pragma unroll
+  for (int i = 0; i < PERIOD; ++i) {
+    const int r = (8 * lane) / DQK, pos = (8 * lane % DQK) / 8;
+    lane_off[i] = (uint32_t)r * rowbytes + (uint32_t)(pos ^ RowSwz<DQK>::f(i * ROWS_REQ + r)) * 16u;
+  }
+  // DMA d (0 <= d < ISS) of this loader's share of tile t: V requests first
+  // (d < V_ISS), then K; request rr of a copy fills its 1 KB block rr
+  auto dma = [&] __device__ (int d, uint32_t toff, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+    const bool isv = d < V_ISS;
+    const int i = isv ? d : d - V_ISS;
+    const int rr = lw * PERIOD + i;
+    attn::dma_chunk(isv ? v_rsrc : k_rsrc, lane_off[i], toff + (uint32_t)(rr * ROWS_REQ) * rowbytes,
+                    (isv ? vdst : kdst) + rr * 512);
+  };
+
+  // per-wave state: S^T and dP^T of the tile between its two phases, dS^T as
+  // bf16 B operands (zero before the first VALU phase), dQ^T accumulators
+  f32x16_t sacc[KB], pacc[KB], dqacc[QBLK];
+  u32x4_t dsb[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) dsb[kb][hh] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int db = 0; db < QBLK; ++db) dqacc[db] = f32x16_t{};
+  const f32x16_t zero = {};
+
+  // A operand of slot s: dQ slots read K_{j-1}^T (two transposing reads),
+  // score slots a K_j row chunk, dP slots a V_j row chunk
+  auto read_op = [&] __device__ (int s, const lds_u16_t* kprev, const lds_u16_t* kcur, const lds_u16_t* vcur)
+      __attribute__((always_inline)) -> bf16x8_t {
+    if (s < NDQ) {
+      const int kb = s / (2 * QBLK), hh = (s / QBLK) % 2, db = s % QBLK;
+      return read_tr<DQK>(kprev, rk, db, kb * 32 + 16 * hh);
+    }
+    if (s < NDQ + NQK) {
+      const int q = s - NDQ, ks = q / KB, kb = q % KB;
+      return read_row<DQK>(kcur, rk, ks, kb);
+    }
+    const int q = s - NDQ - NQK, vs = q / KB, kb = q % KB;
+    return read_row<DV>(vcur, rk, vs, kb);
+  };
+  bf16x8_t op_pre[kPpPrefetch];
+  auto prefetch = [&] __device__ (const lds_u16_t* kprev) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kPpPrefetch; ++s) op_pre[s] = read_op(s, kprev, kprev, kprev);
+  };
+  // one matrix phase; a loader also issues the DMAs of the tile at byte
+  // offset toff into kdst / vdst, one every kDmaStride slots
+  auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* kprev, const lds_u16_t* kcur, const lds_u16_t* vcur,
+                                uint32_t toff, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    bf16x8_t op[NS];
+#pragma unroll
+    for (int s = 0; s < kPpPrefetch; ++s) op[s] = op_pre[s];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + kPpPrefetch < NS) op[s + kPpPrefetch] = read_op(s + kPpPrefetch, kprev, kcur, vcur);
+      if (s < NDQ) {
+        const int kb = s / (2 * QBLK), hh = (s / QBLK) % 2, db = s % QBLK;
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], __builtin_bit_cast(bf16x8_t, dsb[kb][hh]),
+                                                            dqacc[db], 0, 0, 0);
+      } else if (s < NDQ + NQK) {
+        const int q = s - NDQ, ks = q / KB, kb = q % KB;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], qreg[ks], ks == 0 ? zero : sacc[kb], 0, 0, 0);
+      } else {
+        const int q = s - NDQ - NQK, vs = q / KB, kb = q % KB;
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], doreg[vs], vs == 0 ? zero : pacc[kb], 0, 0, 0);
+      }
+      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISS) dma(s / kDmaStride, toff, kdst, vdst);
+    }
+    pin_dq_schedule<0, NS, NDQ>();
+  };
+  // VALU phase of tile t (S^T, dP^T in sacc, pacc): dS = P (dP - D) with the
+  // keys this lane's query does not see masked, as bf16 B operands
+  auto valu = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int k0 = t * kTile;
+    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float ds[16];
+      // keys visible to this lane's query: up to key_lim (offsets within the block)
+      const int lim = masked ? key_lim - (k0 + kb * 32 + 8 * g) : 64;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(sacc[kb][r], c, -lse2) : -__builtin_inff();
+        ds[r] = __builtin_amdgcn_exp2f(x) * (pacc[kb][r] - dq_row);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dsb[kb][hh][jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
+    }
+  };
+
+  // Prologue: K buffer 2 (K_{-1}) zero-filled; the loaders fetch tile 0.
+  for (int i = tid; i < K_ELEMS / 8; i += kDqThreads) ((lds_u32x4_t*)kbuf(2))[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (grp == 0) {
+#pragma unroll
+    for (int d = 0; d < ISS; ++d) dma(d, tile_off(0), kbuf(0), vbuf(0));
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+  using True = GroupTag<true>;
+  using False = GroupTag<false>;
+  auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
+    constexpr bool G0 = decltype(grp_tag)::value;
+    int b0 = 0;                                        // j mod 3
+    if (G0) prefetch(kbuf(2));                         // operands of matrix(0)
+    for (int j = 0; j <= ntiles; ++j) {
+      const int bm1 = (b0 == 0) ? 2 : b0 - 1;          // (j - 1) mod 3
+      const int bp1 = (b0 == 2) ? 0 : b0 + 1;          // (j + 1) mod 3
+      const int vc = j & 1;
+      if (G0) {
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
+        matrix(True{}, kbuf(bm1), kbuf(b0), vbuf(vc), tile_off(j + 1), kbuf(bp1), vbuf(vc ^ 1));
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        attn::barrier();
+        if (j < ntiles) valu(j);
+        prefetch(kbuf(b0));                            // operands of matrix(j+1)
+        attn::dma_wait_barrier<0>();                   // tile j+1 has landed
+      } else {
+        if (j >= 1) valu(j - 1);
+        prefetch(kbuf(bm1));                           // operands of matrix(j)
+        attn::barrier();
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
+        matrix(False{}, kbuf(bm1), kbuf(b0), vbuf(vc), 0u, kbuf(bp1), vbuf(vc ^ 1));
+        if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        attn::barrier();
+      }
+      b0 = bp1;
+    }
+  };
+  if (grp == 0) run(True{});
+  else run(False{});
+  attn::dma_wait_all();
+  block_sync();                                        // the staging area overlaps the tile buffers
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
 
@@ -1066,7 +1324,11 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
   if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
   else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
-  if constexpr (ATTN_BWD_DQ_DMA && DQK == DV && DQK <= 128) {
+  if constexpr (ATTN_BWD_DQ_PP && DQK == DV && DQK <= 128) {
+    const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
+    if (causal) hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
+  } else if constexpr (ATTN_BWD_DQ_DMA && DQK == DV && DQK <= 128) {
     const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
     if (causal) hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
     else hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
