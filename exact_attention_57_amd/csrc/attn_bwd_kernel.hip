@@ -25,11 +25,10 @@
 // for dQ) is staged in LDS once per workgroup and read by all its waves.
 // Every kernel keeps each wave within 256 registers so that each SIMD runs
 // two waves: the dK/dV kernel as one 8-wave workgroup whose two halves split
-// the products between them; the dQ kernel, up to d_qk = 128, as one 8-wave
-// workgroup of 256 queries whose waves each do all three products, in two
-// groups that alternate matrix and VALU phases as the forward kernel does, and
-// at d_qk = 192 as one 8-wave workgroup of 128 queries split like the dK/dV
-// kernel (earlier dQ kernels remain as build options).  The
+// the products between them; the dQ kernel as one 8-wave workgroup of 256
+// queries whose waves each do all three products, in two groups that
+// alternate matrix and VALU phases as the forward kernel does (earlier dQ
+// kernels remain as build options).  The
 // matrix products are v_mfma_f32_32x32x16_bf16 with fp32 accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
@@ -565,10 +564,10 @@ void bwd_dq_dma_kernel(BwdParams p) {
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
 
-// ---- dQ in two ping-pong wave groups (d_qk = d_v <= 128): the forward
-// kernel's schedule applied to the dQ pass.  One workgroup of 8 waves per
-// block of 256 query rows; each wave owns 32 rows (Q and dO as B operands,
-// LSE and D in registers) and runs, per 64-key tile j, a matrix phase -- one
+// ---- dQ in two ping-pong wave groups: the forward kernel's schedule applied
+// to the dQ pass.  One workgroup of 8 waves per block of 256 query rows; each
+// wave owns 32 rows (Q and dO as B operands, LSE and D in registers) and runs,
+// per key tile j (64 keys, 32 at d_qk = 192), a matrix phase -- one
 // stream of MFMAs: dQ^T += K_{j-1}^T dS_{j-1}^T, S^T_j = K_j Q^T,
 // dP^T_j = V_j dO^T -- and a VALU phase: P_j = 2^(c S_j - LSE log2 e) and
 // dS_j = P_j (dP_j - D) as bf16 B operands of the next matrix phase.  Waves
@@ -587,30 +586,81 @@ void bwd_dq_dma_kernel(BwdParams p) {
 // the same code.  The dQ slots come first in the stream: their operands
 // (K_{j-1}, resident since iteration j-2) are read at the end of the wave's
 // previous phase, before the tile DMAs of the current one have landed.
-#ifndef ATTN_BWD_DQ_PP
-#define ATTN_BWD_DQ_PP 1    // 1: the ping-pong dQ kernel at d_qk = d_v <= 128, 0: the 8-wave DMA-fed one
+#ifndef ATTN_BWD_DQ_PP192
+#define ATTN_BWD_DQ_PP192 1 // at d_qk = 192 too (else the two-group split kernel)
 #endif
-constexpr int kPpPrefetch = 4;                        // matrix-phase LDS operands read this many slots ahead
+#ifndef ATTN_BWD_DQ_PP
+#define ATTN_BWD_DQ_PP 1    // 1: the ping-pong dQ kernel (d_qk = 192: ATTN_BWD_DQ_PP192), 0: the earlier ones
+#endif
+// matrix-phase LDS operands read this many slots ahead (fewer at d_qk = 192,
+// whose six dQ blocks leave fewer registers)
+template <int DQK>
+constexpr int pp_prefetch() { return DQK > 128 ? 2 : 4; }
+
+// Per-lane LDS offsets of the row and transposing reads of a row-layout tile,
+// as Reads<D, true>, kept only once per period: for d = 64 and 192 the
+// swizzle values are below 8, so they act within each aligned group of 8
+// chunks and the offsets of k-step s + 4 (column block db + 2) are those of s
+// (db) plus 64 elements; d = 128 has no such period.
+template <int D>
+struct ReadsP {
+  static constexpr bool P8 = (D != 128);
+  static constexpr int NR = P8 && D / 16 > 4 ? 4 : D / 16;
+  static constexpr int NT = P8 && D / 32 > 2 ? 2 : D / 32;
+  int row[NR];
+  int tr[NT];
+  int tr_hi[NT];
+  __device__ ReadsP(int lane) {
+    const int g = lane / 32, sig = sigma(lane % 32);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) row[s] = sig * D + (((2 * s + g) ^ RowSwz<D>::f(sig)) * 8);
+    const int lg = lane / 16, sl = lane % 16, vrow = 8 * (lg / 2) + sl / 4;
+#pragma unroll
+    for (int db = 0; db < NT; ++db) {
+      const int d = db * 32 + 16 * (lg % 2) + 4 * (sl % 4);
+      tr[db] = vrow * D + (((d / 8) ^ RowSwz<D>::f(vrow)) * 8) + (d % 8);
+      tr_hi[db] = (vrow + 4) * D + (((d / 8) ^ RowSwz<D>::f(vrow + 4)) * 8) + (d % 8);
+    }
+  }
+  __device__ int row_at(int s) const { return row[s % NR] + (s / NR) * 64; }
+  __device__ int tr_at(int db) const { return tr[db % NT] + (db / NT) * 64; }
+  __device__ int tr_hi_at(int db) const { return tr_hi[db % NT] + (db / NT) * 64; }
+};
+template <int D>
+__device__ __forceinline__ bf16x8_t read_row_p(const lds_u16_t* tile, const ReadsP<D>& rd, int s, int blk) {
+  return *(const lds_bf16x8_t*)(tile + rd.row_at(s) + blk * 32 * D);
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t read_tr_p(const lds_u16_t* tile, const ReadsP<D>& rd, int db, int r0) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + rd.tr_at(db) + r0 * D));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + rd.tr_hi_at(db) + r0 * D));
+  const i16x4_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+}
 
 // Per slot of the matrix phase: LDS reads issued ahead (two transposing reads
 // for a dQ slot, one 16-byte read otherwise), then the MFMA.
-template <int S, int NS, int NDQ>
+template <int S, int NS, int NDQ, int PF>
 __device__ __forceinline__ void pin_dq_schedule() {
   constexpr int kDsRead = 0x100, kMfma = 0x008;
   if constexpr (S < NS) {
-    if constexpr (S + kPpPrefetch < NS)
-      __builtin_amdgcn_sched_group_barrier(kDsRead, (S + kPpPrefetch < NDQ) ? 2 : 1, 0);
+    if constexpr (S + PF < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, (S + PF < NDQ) ? 2 : 1, 0);
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    pin_dq_schedule<S + 1, NS, NDQ>();
+    pin_dq_schedule<S + 1, NS, NDQ, PF>();
   }
 }
+
+// Keys per tile of the ping-pong dQ kernel: 64, or 32 at d_qk = 192, where
+// the six dQ blocks leave registers for one 32-key block of S and dP.
+template <int DQK>
+constexpr int pp_tile_keys() { return DQK > 128 ? 32 : 64; }
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_pp_kernel(BwdParams p) {
-  static_assert(DQK == DV && DQK <= 128, "ping-pong dQ kernel: d_qk = d_v = 64 or 128");
-  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
-  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
+  constexpr int BK = pp_tile_keys<DQK>();
+  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = BK / 32;
+  constexpr int K_ELEMS = BK * DQK, V_ELEMS = BK * DV;
   constexpr int kKBufs = 3, kVBufs = 2;
   constexpr int TILE_LDS = kKBufs * K_ELEMS + kVBufs * V_ELEMS;
   constexpr int OUT_ELEMS = kDqWaves * kRows * (DQK + 8);
@@ -618,17 +668,23 @@ void bwd_dq_pp_kernel(BwdParams p) {
   static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
   constexpr int kLoaders = kDqWaves / 2;              // group 0 issues the tile DMAs
   constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512;   // 1 KB requests per tile
+  static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0, "whole requests");
   static_assert(K_REQ % kLoaders == 0 && V_REQ % kLoaders == 0, "request split");
   constexpr int K_ISS = K_REQ / kLoaders, V_ISS = V_REQ / kLoaders, ISS = K_ISS + V_ISS;
-  // A 1 KB request covers 512 / D rows; the swizzle of a row depends on its
-  // index mod 16, so a request's lane offsets repeat every D / 32 requests,
-  // and a loader's K_ISS = D / 32 requests per copy need D / 32 of them.
-  constexpr int ROWS_REQ = 512 / DQK, PERIOD = DQK / 32;
-  static_assert(K_ISS == PERIOD && V_ISS == PERIOD, "one lane offset per request of a copy");
+  // When D divides 512, a 1 KB request covers 512 / D whole rows and a row's
+  // swizzle depends on its index mod 16, so a loader's K_ISS = D / 32 requests
+  // per copy need D / 32 lane offsets shared by K and V (d_qk = d_v), with
+  // the requests' row offsets in the uniform soffset; otherwise (d_qk = 192)
+  // each request keeps its own lane offsets.
+  constexpr bool PERIODIC = (512 % DQK == 0) && DQK == DV;
+  constexpr int ROWS_REQ = PERIODIC ? 512 / DQK : 0;
+  constexpr int NOFF = PERIODIC ? K_ISS : ISS;
+  static_assert(!PERIODIC || (K_ISS == DQK / 32 && V_ISS == K_ISS), "one lane offset per request of a copy");
   // matrix-phase slots: dQ (kb, hh, db), then score (ks, kb), then dP (vs, kb)
   constexpr int NDQ = KB * 2 * QBLK, NQK = QK_STEPS * KB, NDP = V_STEPS * KB;
   constexpr int NS = NDQ + NQK + NDP;
-  static_assert(kPpPrefetch <= NDQ, "prefetched slots are dQ slots");
+  constexpr int PF = pp_prefetch<DQK>();
+  static_assert(PF <= NDQ, "prefetched slots are dQ slots");
   constexpr int kDmaStride = NS / ISS;
   static_assert(kDmaStride >= 1, "DMAs per matrix phase");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
@@ -660,39 +716,59 @@ void bwd_dq_pp_kernel(BwdParams p) {
   const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
   const float c = p.c;
 
-  const Reads<DQK, true> rk(lane);                     // K rows and K^T; V rows (d_v = d_qk) alike
+  const ReadsP<DQK> rk(lane);                          // K rows and K^T from the row layout
+  const ReadsP<DV> rv(lane);                           // V rows (the compiler shares rk's when d_v = d_qk)
   const int kend = CAUSAL ? min(L, q0 + kDqBlock) : L;
-  const int ntiles = (kend + kTile - 1) / kTile;
-  const int64_t row_elems = (int64_t)p.H * DQK;        // = H * d_v
-  const uint32_t rowbytes = (uint32_t)(row_elems * 2);
-  const uint32_t seq_bytes = (uint32_t)((L - 1) * row_elems * 2 + DQK * 2);
-  const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * row_elems + (int64_t)h * DQK, seq_bytes);
-  const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * row_elems + (int64_t)h * DV, seq_bytes);
-  // byte offset of tile t; a tile past the last one starts at the resources'
-  // end, so its DMAs return zeros without touching memory
-  auto tile_off = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
-    return t < ntiles ? (uint32_t)(t * kTile) * rowbytes : seq_bytes;
+  const int ntiles = (kend + BK - 1) / BK;
+  const int64_t k_row = (int64_t)p.H * DQK, v_row = (int64_t)p.H * DV;     // elements per token
+  const uint32_t k_rowbytes = (uint32_t)(k_row * 2), v_rowbytes = (uint32_t)(v_row * 2);
+  const uint32_t k_bytes = (uint32_t)((L - 1) * k_row * 2 + DQK * 2);
+  const uint32_t v_bytes = (uint32_t)((L - 1) * v_row * 2 + DV * 2);
+  const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * k_row + (int64_t)h * DQK, k_bytes);
+  const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_row + (int64_t)h * DV, v_bytes);
+  // byte offsets of tile t in K and V; a tile past the last one starts at
+  // the resources' end, so its DMAs return zeros without touching memory
+  auto k_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BK) * k_rowbytes : k_bytes;
   };
-  // Lane offsets of a copy's request rr = lw * PERIOD + i (its rows from
-  // rr * ROWS_REQ on; the row offset goes into the uniform soffset): lane l
-  // writes the 16 bytes at LDS position 8 l of the request's 1 KB block, i.e.
-  // chunk `pos` of row rr * ROWS_REQ + r, which holds the tile's chunk
-  // pos ^ f(row) of that row.  f depends on the row mod 16, and
-  // PERIOD * ROWS_REQ = 16, so it depends on i, not on lw.
-  uint32_t lane_off[PERIOD];
+  auto v_tile = [&] __device__ (int t) __attribute__((always_inline)) -> uint32_t {
+    return t < ntiles ? (uint32_t)(t * BK) * v_rowbytes : v_bytes;
+  };
+  // Lane offsets: request rr of a copy fills its 1 KB block rr; lane l writes
+  // the 16 bytes at LDS position 8 l of the block, i.e. chunk `pos` of tile
+  // row `row`, which holds the tile's chunk pos ^ f(row) of that row.  In the
+  // periodic case the offset of request i keeps only the row within the
+  // request (the request's first row, rr * ROWS_REQ with rr = lw * K_ISS + i,
+  // goes into soffset); f depends on the row mod 16 and K_ISS * ROWS_REQ = 16,
+  // so it depends on i, not on lw.
+  uint32_t lane_off[NOFF];
 #pragma unroll
-  for (int i = 0; i < PERIOD; ++i) {
-    const int r = (8 * lane) / DQK, pos = (8 * lane % DQK) / 8;
-    lane_off[i] = (uint32_t)r * rowbytes + (uint32_t)(pos ^ RowSwz<DQK>::f(i * ROWS_REQ + r)) * 16u;
+  for (int i = 0; i < NOFF; ++i) {
+    if constexpr (PERIODIC) {
+      const int r = (8 * lane) / DQK, pos = (8 * lane % DQK) / 8;
+      lane_off[i] = (uint32_t)r * k_rowbytes + (uint32_t)(pos ^ RowSwz<DQK>::f(i * ROWS_REQ + r)) * 16u;
+    } else {
+      const bool isv = i < V_ISS;
+      const int rr = isv ? lw * V_ISS + i : lw * K_ISS + (i - V_ISS);
+      const int D = isv ? DV : DQK;
+      const int e = rr * 512 + 8 * lane, row = e / D, pos = (e % D) / 8;
+      const int f = isv ? RowSwz<DV>::f(row) : RowSwz<DQK>::f(row);
+      lane_off[i] = (uint32_t)row * (isv ? v_rowbytes : k_rowbytes) + (uint32_t)(pos ^ f) * 16u;
+    }
   }
   // DMA d (0 <= d < ISS) of this loader's share of tile t: V requests first
-  // (d < V_ISS), then K; request rr of a copy fills its 1 KB block rr
-  auto dma = [&] __device__ (int d, uint32_t toff, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+  // (d < V_ISS), then K
+  auto dma = [&] __device__ (int d, int t, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
     const bool isv = d < V_ISS;
     const int i = isv ? d : d - V_ISS;
-    const int rr = lw * PERIOD + i;
-    attn::dma_chunk(isv ? v_rsrc : k_rsrc, lane_off[i], toff + (uint32_t)(rr * ROWS_REQ) * rowbytes,
-                    (isv ? vdst : kdst) + rr * 512);
+    const int rr = lw * (isv ? V_ISS : K_ISS) + i;
+    if constexpr (PERIODIC) {
+      attn::dma_chunk(isv ? v_rsrc : k_rsrc, lane_off[i],
+                      (isv ? v_tile(t) : k_tile(t)) + (uint32_t)(rr * ROWS_REQ) * (isv ? v_rowbytes : k_rowbytes),
+                      (isv ? vdst : kdst) + rr * 512);
+    } else {
+      attn::dma_chunk(isv ? v_rsrc : k_rsrc, lane_off[d], isv ? v_tile(t) : k_tile(t), (isv ? vdst : kdst) + rr * 512);
+    }
   };
 
   // per-wave state: S^T and dP^T of the tile between its two phases, dS^T as
@@ -713,31 +789,32 @@ void bwd_dq_pp_kernel(BwdParams p) {
       __attribute__((always_inline)) -> bf16x8_t {
     if (s < NDQ) {
       const int kb = s / (2 * QBLK), hh = (s / QBLK) % 2, db = s % QBLK;
-      return read_tr<DQK>(kprev, rk, db, kb * 32 + 16 * hh);
+      return read_tr_p<DQK>(kprev, rk, db, kb * 32 + 16 * hh);
     }
     if (s < NDQ + NQK) {
       const int q = s - NDQ, ks = q / KB, kb = q % KB;
-      return read_row<DQK>(kcur, rk, ks, kb);
+      return read_row_p<DQK>(kcur, rk, ks, kb);
     }
     const int q = s - NDQ - NQK, vs = q / KB, kb = q % KB;
-    return read_row<DV>(vcur, rk, vs, kb);
+    if constexpr (DV == DQK) return read_row_p<DV>(vcur, rk, vs, kb);
+    else return read_row_p<DV>(vcur, rv, vs, kb);
   };
-  bf16x8_t op_pre[kPpPrefetch];
+  bf16x8_t op_pre[PF];
   auto prefetch = [&] __device__ (const lds_u16_t* kprev) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < kPpPrefetch; ++s) op_pre[s] = read_op(s, kprev, kprev, kprev);
+    for (int s = 0; s < PF; ++s) op_pre[s] = read_op(s, kprev, kprev, kprev);
   };
-  // one matrix phase; a loader also issues the DMAs of the tile at byte
-  // offset toff into kdst / vdst, one every kDmaStride slots
+  // one matrix phase; a loader also issues the DMAs of tile tn into kdst /
+  // vdst, one every kDmaStride slots
   auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* kprev, const lds_u16_t* kcur, const lds_u16_t* vcur,
-                                uint32_t toff, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
+                                int tn, lds_u16_t* kdst, lds_u16_t* vdst) __attribute__((always_inline)) {
     constexpr bool DMA = decltype(dma_tag)::value;
     bf16x8_t op[NS];
 #pragma unroll
-    for (int s = 0; s < kPpPrefetch; ++s) op[s] = op_pre[s];
+    for (int s = 0; s < PF; ++s) op[s] = op_pre[s];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s + kPpPrefetch < NS) op[s + kPpPrefetch] = read_op(s + kPpPrefetch, kprev, kcur, vcur);
+      if (s + PF < NS) op[s + PF] = read_op(s + PF, kprev, kcur, vcur);
       if (s < NDQ) {
         const int kb = s / (2 * QBLK), hh = (s / QBLK) % 2, db = s % QBLK;
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], __builtin_bit_cast(bf16x8_t, dsb[kb][hh]),
@@ -749,15 +826,15 @@ void bwd_dq_pp_kernel(BwdParams p) {
         const int q = s - NDQ - NQK, vs = q / KB, kb = q % KB;
         pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s], doreg[vs], vs == 0 ? zero : pacc[kb], 0, 0, 0);
       }
-      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISS) dma(s / kDmaStride, toff, kdst, vdst);
+      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISS) dma(s / kDmaStride, tn, kdst, vdst);
     }
-    pin_dq_schedule<0, NS, NDQ>();
+    pin_dq_schedule<0, NS, NDQ, PF>();
   };
   // VALU phase of tile t (S^T, dP^T in sacc, pacc): dS = P (dP - D) with the
   // keys this lane's query does not see masked, as bf16 B operands
   auto valu = [&] __device__ (int t) __attribute__((always_inline)) {
-    const int k0 = t * kTile;
-    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
+    const int k0 = t * BK;
+    const bool masked = (k0 + BK > L) || (qw0 + kRows > L) || (CAUSAL && k0 + BK - 1 > qw0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       float ds[16];
@@ -779,7 +856,7 @@ void bwd_dq_pp_kernel(BwdParams p) {
   for (int i = tid; i < K_ELEMS / 8; i += kDqThreads) ((lds_u32x4_t*)kbuf(2))[i] = u32x4_t{0u, 0u, 0u, 0u};
   if (grp == 0) {
 #pragma unroll
-    for (int d = 0; d < ISS; ++d) dma(d, tile_off(0), kbuf(0), vbuf(0));
+    for (int d = 0; d < ISS; ++d) dma(d, 0, kbuf(0), vbuf(0));
   }
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -796,7 +873,7 @@ void bwd_dq_pp_kernel(BwdParams p) {
       const int vc = j & 1;
       if (G0) {
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
-        matrix(True{}, kbuf(bm1), kbuf(b0), vbuf(vc), tile_off(j + 1), kbuf(bp1), vbuf(vc ^ 1));
+        matrix(True{}, kbuf(bm1), kbuf(b0), vbuf(vc), j + 1, kbuf(bp1), vbuf(vc ^ 1));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         attn::barrier();
         if (j < ntiles) valu(j);
@@ -807,7 +884,7 @@ void bwd_dq_pp_kernel(BwdParams p) {
         prefetch(kbuf(bm1));                           // operands of matrix(j)
         attn::barrier();
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_SETPRIO);
-        matrix(False{}, kbuf(bm1), kbuf(b0), vbuf(vc), 0u, kbuf(bp1), vbuf(vc ^ 1));
+        matrix(False{}, kbuf(bm1), kbuf(b0), vbuf(vc), 0, kbuf(bp1), vbuf(vc ^ 1));
         if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         attn::barrier();
       }
@@ -1324,7 +1401,7 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
   if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
   else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
-  if constexpr (ATTN_BWD_DQ_PP && DQK == DV && DQK <= 128) {
+  if constexpr (ATTN_BWD_DQ_PP && (DQK <= 128 || ATTN_BWD_DQ_PP192)) {
     const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
     if (causal) hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
     else hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
