@@ -435,7 +435,6 @@ constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * kWave;
 constexpr int kDqBlock = kDqWaves * kRows;           // query rows per workgroup
 
-int dq_dma_block_rows() { return kDqBlock; }
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
