@@ -80,13 +80,23 @@ def test_ragged_packed_all_elements(dims, causal):
     full_check(inp, causal, 1.0 / np.sqrt(dims[0]), f"packed ragged d{dims}")
 
 
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sequences_ending_on_tile_and_block_boundaries(dims, causal):
+    """Sequence ends exactly at multiples of the key tiles (32, 64), the
+    128-key dK/dV block and the 256-query dQ block, so the tile after a
+    sequence's last one lies wholly past its end."""
+    inp = workloads.make_custom_inputs([256, 32, 64, 512, 128], 2, dims[0], dims[1], seed=21)
+    full_check(inp, causal, 1.0 / np.sqrt(dims[0]), f"boundary-length sequences d{dims}", packed=True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fixed_length_ragged_tail(causal):
     inp = workloads.make_custom_inputs([300, 300], 2, 128, 128, seed=5)
     full_check(inp, causal, 1.0 / np.sqrt(128), "fixed N300 d128", packed=False)
 
 
-@pytest.mark.parametrize("dims", [(64, 64), (192, 128)])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
 def test_empty_and_single_token_sequences(dims):
     inp = workloads.make_custom_inputs([0, 1, 0, 64, 5], 3, dims[0], dims[1], seed=7)
     full_check(inp, True, 1.0 / np.sqrt(dims[0]), f"empty and single-token sequences d{dims}", packed=True)
