@@ -21,20 +21,23 @@
 // results are bitwise reproducible run to run.
 //
 // Layout of the work on the chip: each wave owns 32 rows of its workgroup's
-// block; a 64-row tile of the streamed operands (Q and dO for dK/dV, K and V
-// for dQ) is staged in LDS once per workgroup and read by all its waves.
-// Every kernel keeps each wave within 256 registers so that each SIMD runs
-// two waves: the dK/dV kernel as one 8-wave workgroup whose two halves split
-// the products between them; the dQ kernel as one 8-wave workgroup of 256
-// queries whose waves each do all three products, in two groups that
-// alternate matrix and VALU phases as the forward kernel does (earlier dQ
-// kernels remain as build options).  The
-// matrix products are v_mfma_f32_32x32x16_bf16 with fp32 accumulators:
+// block; the streamed operands (Q and dO for dK/dV, K and V for dQ) are
+// staged in LDS once per workgroup and read by all its waves.  Every kernel
+// keeps each wave within 256 registers so that each SIMD runs two waves, in
+// two groups that alternate matrix and VALU phases as the forward kernel
+// does: the dQ kernel as one 8-wave workgroup of 256 queries whose waves each
+// do all three products; the dK/dV kernel, up to d = 128, as one 8-wave
+// workgroup of 128 keys whose two groups split the query blocks, with K and V
+// read from LDS, and at (192, 128) as one 8-wave workgroup whose two halves
+// split the products between them (earlier kernels remain as build
+// options).  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
-//   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V in registers)
-//               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read),
-//               S, P, dV^T in one wave group and dP, dS, dK^T in the other
+//   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V rows from LDS
+//                                               up to d = 128, in registers at (192, 128))
+//               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read);
+//               at (192, 128) S, P, dV^T in one wave group and dP, dS, dK^T in the other
 // With the streamed tile's rows read in an order with bits 2 and 3 of the
 // row index swapped, accumulator registers 0..7 and 8..15 of a 32 x 32
 // block hold 8 consecutive rows -- the B-operand slots of the next product --
@@ -57,6 +60,7 @@ namespace attn_grad {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -71,6 +75,7 @@ typedef __attribute__((address_space(3))) float lds_f32_t;
 constexpr int kWave = 64;
 constexpr int kWaves = 4;                     // one per SIMD
 constexpr int kThreads = kWave * kWaves;
+constexpr int kThreads2 = 2 * kThreads;              // the 8-wave (two-group) kernels
 constexpr int kRows = 32;                     // block rows per wave
 constexpr int kBlock = kRows * kWaves;        // block rows per workgroup
 constexpr int kTile = 64;                     // streamed rows per LDS tile
@@ -897,6 +902,319 @@ void bwd_dq_pp_kernel(BwdParams p) {
   store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
 }
 
+// ---- dK, dV in two ping-pong wave groups (d_qk = d_v <= 128): the dQ
+// kernel's schedule with the roles of queries and keys swapped.  One
+// workgroup of 8 waves per block of 128 keys; waves 0-3 (group 0) and 4-7
+// (group 1) own the same four 32-key slices and split the 32-query blocks,
+// group 0 taking the even blocks and group 1 the odd ones, each with its own
+// dK^T and dV^T accumulators (summed through LDS at the end).  K and V of the
+// workgroup's keys stay in LDS (64 KB at d = 128) and are read as the B
+// operands of S = Q K^T and dP = dO V^T, so a wave's registers hold only its
+// accumulators and one block's S, dP, P and dS.  Per block b of its group a
+// wave runs a matrix phase -- dV^T += dO_{b-2}^T P_{b-2}, dK^T += Q_{b-2}^T
+// dS_{b-2}, S_b, dP_b, one pinned stream of MFMAs -- and a VALU phase (P_b
+// from the LSE, dS_b = P_b (dP_b - D) as bf16 B operands); the two groups run
+// half an iteration apart between workgroup barriers, so one group's MFMAs
+// run beside the other's VALU work:
+//   group 0: | matrix(2j)   | VALU(2j)     | matrix(2j+2) ...
+//   group 1: | VALU(2j-1)   | matrix(2j+1) | VALU(2j+1)   ...
+// Query blocks (Q, dO, and their LSE and D rows) rotate through five LDS
+// slots, block b in slot b mod 5.  During its matrix phase of iteration j a
+// group fetches its block two ahead (group 0: 2j+2, group 1: 2j+3), into the
+// slot whose block was last read earlier in the same iteration or before;
+// group 0 waits for it before the barrier that ends iteration j, group 1
+// before the mid barrier of iteration j+1.  Blocks -2 and -1 are zero-filled
+// slots multiplied by zero P and dS; blocks past the sequence end read zeros
+// and are masked.
+#ifndef ATTN_BWD_DKDV_PP
+#define ATTN_BWD_DKDV_PP 1  // 1: this kernel at d_qk = d_v <= 128, 0: the two-group split kernel
+#endif
+constexpr int kKvPrefetch = 4;                       // matrix-phase slots whose operands are read ahead
+
+template <int S, int NS, int NTR>
+__device__ __forceinline__ void pin_kv_schedule() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  if constexpr (S < NS) {
+    // a dV / dK slot reads one transposed operand (two reads), an S / dP slot
+    // an A and a B operand (two reads)
+    if constexpr (S + kKvPrefetch < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    pin_kv_schedule<S + 1, NS, NTR>();
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_pp_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "ping-pong dK/dV kernel: d_qk = d_v = 64 or 128");
+  constexpr int STEPS = D / 16, BLKS = D / 32;
+  constexpr int KV_ELEMS = kBlock * D;                            // K (then V) rows of the workgroup
+  constexpr int QD_ELEMS = kRows * D;                             // one query block of Q (then dO)
+  constexpr int ROWS_OFF = 2 * QD_ELEMS;                          // 64 LSE values, then 64 D values (fp32)
+  constexpr int SLOT_ELEMS = (ROWS_OFF + 2 * 64 * 2 + 511) / 512 * 512;
+  constexpr int kSlots = 5;
+  constexpr int SLOTS_OFF = 2 * KV_ELEMS;
+  constexpr int LOOP_ELEMS = SLOTS_OFF + kSlots * SLOT_ELEMS;
+  constexpr int MERGE_ELEMS = kWaves * kWave * 2 * BLKS * 16 * 2; // group 1's dK^T and dV^T, fp32
+  // a group-0 wave stages its output rows in its own merge region once it has read it
+  static_assert(2 * kRows * (D + 8) <= kWave * 2 * BLKS * 16 * 2, "staging inside a wave's merge region");
+  constexpr int LDS_ELEMS = LOOP_ELEMS > MERGE_ELEMS ? LOOP_ELEMS : MERGE_ELEMS;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
+  constexpr int ROWS_REQ = 512 / D;                               // rows per 1 KB request
+  constexpr int KV_REQ = KV_ELEMS / 512;                          // requests per K or V copy
+  constexpr int KV_ISS = 2 * KV_REQ / (2 * kWaves);               // per wave, K and V
+  constexpr int B_REQ = QD_ELEMS / 512;                           // requests per Q or dO block
+  static_assert(B_REQ % kWaves == 0 && (2 * KV_REQ) % (2 * kWaves) == 0, "request split");
+  constexpr int B_ISS = B_REQ / kWaves;                           // per wave per copy of a block
+  constexpr int ISS = 2 * B_ISS + 1;                              // Q, dO, and one LSE or D request
+  // matrix-phase slots: dV (hh, db), dK (hh, db), S (ks), dP (ks)
+  constexpr int NDV = 2 * BLKS, NTR = 2 * NDV, NS = NTR + 2 * STEPS;
+  constexpr int kDmaStride = NS / ISS;
+  static_assert(kDmaStride >= 1, "DMAs per matrix phase");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
+  lds_u16_t* const lds = (lds_u16_t*)smem;
+  auto slot = [&] __device__ (int i) __attribute__((always_inline)) { return lds + SLOTS_OFF + i * SLOT_ELEMS; };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave / kWaves, wv = wave % kWaves;
+  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
+  int h, b, blk;
+  decode_block(p, false, h, b, blk);
+  int seq0, L;
+  seq_range(p, b, seq0, L);
+  const int k0 = blk * kBlock;
+  if (k0 >= L) return;                                            // uniform over the workgroup
+  const int kw0 = k0 + wv * kRows;
+  const int key = kw0 + lq;
+  const bool key_valid = key < L;
+  const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
+  const int nblk = (L - qstart + kRows - 1) / kRows;              // 32-query blocks
+  const int niter = (nblk + 1) / 2;                               // iterations 0..niter
+  const int64_t row = (int64_t)p.H * D;
+  const uint32_t rowbytes = (uint32_t)(row * 2);
+  const uint32_t seq_bytes = (uint32_t)((L - 1) * row * 2 + D * 2);
+  const int T = total_tokens(p);
+  const attn::u32x4_t q_rsrc = attn::make_rsrc(p.q + (int64_t)seq0 * row + (int64_t)h * D, seq_bytes);
+  const attn::u32x4_t o_rsrc = attn::make_rsrc(p.dout + (int64_t)seq0 * row + (int64_t)h * D, seq_bytes);
+  const attn::u32x4_t l_rsrc = attn::make_rsrc(p.lse + (int64_t)h * T + seq0, (uint32_t)L * 4u);
+  const attn::u32x4_t d_rsrc = attn::make_rsrc(p.delta + (int64_t)h * T + seq0, (uint32_t)L * 4u);
+  const float c = p.c;
+
+  // K and V of the workgroup's keys into LDS (rows past L read zeros)
+  {
+    const uint32_t kv_bytes = (uint32_t)(L - 1 - k0) * rowbytes + (uint32_t)(D * 2);
+    const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)(seq0 + k0) * row + (int64_t)h * D, kv_bytes);
+    const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)(seq0 + k0) * row + (int64_t)h * D, kv_bytes);
+#pragma unroll
+    for (int i = 0; i < KV_ISS; ++i) {
+      const int r = wave * KV_ISS + i, isv = r >= KV_REQ, rr = isv ? r - KV_REQ : r;
+      const int e = rr * 512 + 8 * lane, krow = e / D, pos = (e % D) / 8;
+      const uint32_t off = (uint32_t)krow * rowbytes + (uint32_t)(pos ^ RowSwz<D>::f(krow)) * 16u;
+      attn::dma_chunk(isv ? v_rsrc : k_rsrc, off, 0u, lds + (isv ? KV_ELEMS : 0) + rr * 512);
+    }
+  }
+  // per-lane offsets of this wave's K and V rows (B operands: row = key, not
+  // the bit-swapped order), k-step ks
+  int kvoff[STEPS];
+#pragma unroll
+  for (int ks = 0; ks < STEPS; ++ks) {
+    const int r = wv * kRows + lq;
+    kvoff[ks] = r * D + (((2 * ks + g) ^ RowSwz<D>::f(r)) * 8);
+  }
+  const ReadsP<D> rq(lane);                                       // Q, dO rows and Q^T, dO^T of a block
+
+  // query-block DMAs: request rr of the Q or dO copy fills 1 KB block rr of
+  // the slot (rows rr * ROWS_REQ on, in soffset); lane offsets depend on rr
+  // mod (16 / ROWS_REQ) through the swizzle, and this wave's requests are
+  // rr = wv * B_ISS + i
+  uint32_t lane_off[B_ISS];
+#pragma unroll
+  for (int i = 0; i < B_ISS; ++i) {
+    const int rr = wv * B_ISS + i, r = (8 * lane) / D, pos = (8 * lane % D) / 8;
+    lane_off[i] = (uint32_t)r * rowbytes + (uint32_t)(pos ^ RowSwz<D>::f(rr * ROWS_REQ + r)) * 16u;
+  }
+  auto block_off = [&] __device__ (int bq) __attribute__((always_inline)) -> uint32_t {
+    return bq < nblk ? (uint32_t)(qstart + bq * kRows) * rowbytes : seq_bytes;
+  };
+  // DMA d of this wave's share of block bq into slot dst: Q, dO, then the
+  // LSE (waves 0, 2) or D (waves 1, 3) rows, 64 values from the block's first
+  // row (only the first 32 are read)
+  auto dma = [&] __device__ (int d, int bq, lds_u16_t* dst) __attribute__((always_inline)) {
+    if (d < 2 * B_ISS) {
+      const bool iso = d >= B_ISS;
+      const int i = iso ? d - B_ISS : d, rr = wv * B_ISS + i;
+      attn::dma_chunk(iso ? o_rsrc : q_rsrc, lane_off[i], block_off(bq) + (uint32_t)(rr * ROWS_REQ) * rowbytes,
+                      dst + (iso ? QD_ELEMS : 0) + rr * 512);
+    } else if (wv < 2) {
+      const uint32_t r0 = bq < nblk ? (uint32_t)(qstart + bq * kRows) * 4u : (uint32_t)L * 4u;
+      attn::dma_dword(wv == 0 ? l_rsrc : d_rsrc, r0 + 4u * lane, dst + ROWS_OFF + wv * 128);
+    }
+  };
+
+  f32x16_t dk[BLKS], dv[BLKS];
+#pragma unroll
+  for (int i = 0; i < BLKS; ++i) { dk[i] = f32x16_t{}; dv[i] = f32x16_t{}; }
+  f32x16_t sacc = {}, pacc = {};
+  u32x4_t pb[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+  u32x4_t dsb[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+  const f32x16_t zero = {};
+
+  // A and B operands of slot s: dV / dK slots read block bprev transposed
+  // (B is P or dS in registers), S / dP slots a row chunk of block bcur and
+  // of this wave's K or V rows
+  struct Ops { bf16x8_t a, b; };
+  auto read_op = [&] __device__ (int s, const lds_u16_t* sprev, const lds_u16_t* scur) __attribute__((always_inline))
+      -> Ops {
+    Ops o;
+    if (s < NTR) {
+      const int isk = s >= NDV, q = isk ? s - NDV : s, hh = q / BLKS, db = q % BLKS;
+      o.a = read_tr_p<D>(sprev + (isk ? 0 : QD_ELEMS), rq, db, 16 * hh);
+      o.b = o.a;
+    } else {
+      const int q = s - NTR, isdp = q >= STEPS, ks = isdp ? q - STEPS : q;
+      o.a = read_row_p<D>(scur + (isdp ? QD_ELEMS : 0), rq, ks, 0);
+      o.b = *(const lds_bf16x8_t*)(lds + (isdp ? KV_ELEMS : 0) + kvoff[ks]);
+    }
+    return o;
+  };
+  Ops op_pre[kKvPrefetch];
+  auto prefetch = [&] __device__ (const lds_u16_t* sprev) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kKvPrefetch; ++s) op_pre[s] = read_op(s, sprev, sprev);
+  };
+  // matrix phase on blocks bprev (dV, dK) and bcur (S, dP); with DMA the
+  // wave issues its share of block bnext into slot dst
+  auto matrix = [&] __device__ (auto dma_tag, const lds_u16_t* sprev, const lds_u16_t* scur, int bnext,
+                                lds_u16_t* dst) __attribute__((always_inline)) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    Ops op[NS];
+#pragma unroll
+    for (int s = 0; s < kKvPrefetch; ++s) op[s] = op_pre[s];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + kKvPrefetch < NS) op[s + kKvPrefetch] = read_op(s + kKvPrefetch, sprev, scur);
+      if (s < NTR) {
+        const int isk = s >= NDV, q = isk ? s - NDV : s, hh = q / BLKS, db = q % BLKS;
+        if (isk) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, __builtin_bit_cast(bf16x8_t, dsb[hh]), dk[db], 0, 0, 0);
+        else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, __builtin_bit_cast(bf16x8_t, pb[hh]), dv[db], 0, 0, 0);
+      } else {
+        const int q = s - NTR, isdp = q >= STEPS, ks = isdp ? q - STEPS : q;
+        if (isdp) pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, op[s].b, ks == 0 ? zero : pacc, 0, 0, 0);
+        else sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, op[s].b, ks == 0 ? zero : sacc, 0, 0, 0);
+      }
+      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISS) dma(s / kDmaStride, bnext, dst);
+    }
+    pin_kv_schedule<0, NS, NTR>();
+  };
+  // VALU phase of block bq (S, dP in sacc, pacc; LSE and D rows in its slot)
+  auto valu = [&] __device__ (int bq, const lds_u16_t* sq) __attribute__((always_inline)) {
+    const lds_f32_t* const lse_s = (const lds_f32_t*)(sq + ROWS_OFF);
+    const lds_f32_t* const d_s = lse_s + 64;
+    const int q_base = qstart + bq * kRows;
+    const bool masked = (q_base + kRows > L) || (kw0 + kRows > L) || (CAUSAL && kw0 + kRows - 1 > q_base) || bq < 0;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 16 * (r / 8) + 8 * g + (r % 8);
+      x[r] = __builtin_fmaf(sacc[r], c, -lse_s[qi] * kLog2e);
+    }
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int query = q_base + 16 * (r / 8) + 8 * g + (r % 8);
+        if (!(key_valid && bq >= 0 && query < L && (!CAUSAL || key <= query))) x[r] = -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 8 * hh + 2 * jj, qi = 16 * hh + 8 * g + 2 * jj;
+        const float p0 = __builtin_amdgcn_exp2f(x[r]), p1 = __builtin_amdgcn_exp2f(x[r + 1]);
+        pb[hh][jj] = pack_bf16x2(p0, p1);
+        dsb[hh][jj] = pack_bf16x2(p0 * (pacc[r] - d_s[qi]), p1 * (pacc[r + 1] - d_s[qi + 1]));
+      }
+  };
+
+  // Prologue: slots 3 and 4 (blocks -2, -1) zeros; blocks 0 and 1.
+  for (int i = tid; i < 2 * SLOT_ELEMS / 8; i += kThreads2) ((lds_u32x4_t*)slot(3))[i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int d = 0; d < ISS; ++d) {
+    dma(d, 0 + grp, slot(grp));                                   // group 0: block 0, group 1: block 1
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+  using True = GroupTag<true>;
+  using False = GroupTag<false>;
+  auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
+    constexpr bool G0 = decltype(grp_tag)::value;
+    int c0 = 0;                                                   // (2j) mod 5
+    if (G0) prefetch(slot(3));                                    // matrix(0): block -2
+    for (int j = 0; j <= niter; ++j) {
+      auto m5 = [&] __device__ (int a) __attribute__((always_inline)) { return a >= 5 ? a - 5 : a; };
+      const int s_even = c0, s_odd = m5(c0 + 1), s_even_m2 = m5(c0 + 3), s_odd_m2 = m5(c0 + 4);
+      const int s_even_p2 = m5(c0 + 2), s_odd_p2 = m5(c0 + 3);
+      if (G0) {
+        __builtin_amdgcn_s_setprio(1);
+        matrix(True{}, slot(s_even_m2), slot(s_even), 2 * j + 2, slot(s_even_p2));
+        __builtin_amdgcn_s_setprio(0);
+        attn::barrier();
+        valu(2 * j, slot(s_even));
+        prefetch(slot(s_even));                                   // matrix(2j+2) starts with block 2j
+        attn::dma_wait_barrier<0>();                              // block 2j+2 has landed
+      } else {
+        valu(2 * j - 1, slot(s_odd_m2));
+        prefetch(slot(s_odd_m2));                                 // matrix(2j+1) starts with block 2j-1
+        attn::dma_wait_barrier<0>();                              // block 2j+1 has landed
+        __builtin_amdgcn_s_setprio(1);
+        matrix(True{}, slot(s_odd_m2), slot(s_odd), 2 * j + 3, slot(s_odd_p2));
+        __builtin_amdgcn_s_setprio(0);
+        attn::barrier();
+      }
+      c0 = m5(c0 + 2);
+    }
+  };
+  if (grp == 0) run(True{});
+  else run(False{});
+  attn::dma_wait_all();
+  block_sync();
+  // group 1's partial dK^T, dV^T -> LDS (16-byte pieces, lane-interleaved);
+  // group 0 adds them and stores dK (times the scale) and dV
+  lds_f32_t* const merge = (lds_f32_t*)lds + wv * (kWave * 2 * BLKS * 16);
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < BLKS; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t a = {dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2], dk[db][4 * q4 + 3]};
+        const f32x4_t v = {dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+        *(__attribute__((address_space(3))) f32x4_t*)(merge + ((db * 4 + q4) * kWave + lane) * 4) = a;
+        *(__attribute__((address_space(3))) f32x4_t*)(merge + (((BLKS + db) * 4 + q4) * kWave + lane) * 4) = v;
+      }
+  }
+  block_sync();
+  if (grp == 0) {
+#pragma unroll
+    for (int db = 0; db < BLKS; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t a = *(const __attribute__((address_space(3))) f32x4_t*)(merge + ((db * 4 + q4) * kWave + lane) * 4);
+        const f32x4_t v = *(const __attribute__((address_space(3))) f32x4_t*)(merge + (((BLKS + db) * 4 + q4) * kWave + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[db][4 * q4 + e] += a[e];
+          dv[db][4 * q4 + e] += v[e];
+        }
+      }
+    // the wave's own merge region, read above, stages its dK and dV rows
+    lds_u16_t* const stage = (lds_u16_t*)merge;
+    store_rows<D>(dk, p.scale, stage, p.dk, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+    store_rows<D>(dv, 1.0f, stage + kRows * (D + 8), p.dv, (int64_t)seq0 + kw0, L - kw0, p.H, h, lane);
+  }
+}
+
 // ---- dK, dV with the work split over two wave groups: one workgroup of 8
 // waves per block of 128 key rows.  Waves 0-3 (dV group) own 32 keys each and
 // compute S = Q K^T, P and dV^T += dO^T P; waves 4-7 (dK group) own the same
@@ -910,7 +1228,6 @@ void bwd_dq_pp_kernel(BwdParams p) {
 //   dV group: ... | dV(b), S(b+1), P(b+1) -> LDS | dV(b+1), S(b+2) ...
 //   dK group: ... | dS(b), dK(b), dP(b+1)       | dS(b+1), dK(b+1) ...
 // P alternates between two LDS buffers, the Q/dO tiles between two more.
-constexpr int kThreads2 = 2 * kThreads;
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_split_kernel(BwdParams p) {
@@ -1398,8 +1715,13 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   constexpr int RPB = kThreads / (DV / 8);
   hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, s, p);
   const dim3 grid((unsigned)p.B * p.H * p.n_blocks);
-  if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
-  else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
+  if constexpr (ATTN_BWD_DKDV_PP && DQK == DV && DQK <= 128) {
+    if (causal) hipLaunchKernelGGL((bwd_dkdv_pp_kernel<DQK, true>), grid, dim3(kThreads2), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkdv_pp_kernel<DQK, false>), grid, dim3(kThreads2), 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
+  }
   if constexpr (ATTN_BWD_DQ_PP && (DQK <= 128 || ATTN_BWD_DQ_PP192)) {
     const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
     if (causal) hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
