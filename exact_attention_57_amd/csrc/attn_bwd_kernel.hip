@@ -1103,7 +1103,8 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
         if (isdp) pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, op[s].b, ks == 0 ? zero : pacc, 0, 0, 0);
         else sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[s].a, op[s].b, ks == 0 ? zero : sacc, 0, 0, 0);
       }
-      if (DMA && s % kDmaStride == kDmaStride / 2 && s / kDmaStride < ISS) dma(s / kDmaStride, bnext, dst);
+      // a request after the last MFMA of each stride of slots (measured: mid-stride −0.5 %, first slot −1.5 %)
+      if (DMA && s % kDmaStride == kDmaStride - 1 && s / kDmaStride < ISS) dma(s / kDmaStride, bnext, dst);
     }
     pin_kv_schedule<0, NS, NTR>();
   };
