@@ -908,11 +908,13 @@ void bwd_dq_pp_kernel(BwdParams p) {
 // (group 1) own the same four 32-key slices and split the 32-query blocks,
 // group 0 taking the even blocks and group 1 the odd ones, each with its own
 // dK^T and dV^T accumulators (summed through LDS at the end).  K and V of the
-// workgroup's keys stay in LDS (64 KB at d = 128) and are read as the B
-// operands of S = Q K^T and dP = dO V^T, so a wave's registers hold only its
-// accumulators and one block's S, dP, P and dS.  Per block b of its group a
-// wave runs a matrix phase -- dV^T += dO_{b-2}^T P_{b-2}, dK^T += Q_{b-2}^T
-// dS_{b-2}, S_b, dP_b, one pinned stream of MFMAs -- and a VALU phase (P_b
+// workgroup's keys land in LDS (64 KB at d = 128); each wave copies its 32 K
+// rows into registers once (the B operands of S = Q K^T, 32 VGPRs at d = 128)
+// and reads V from LDS as the B operand of dP = dO V^T, so a wave's registers
+// hold its accumulators, its K rows and one block's S, dP, P and dS.  Per
+// block b of its group a wave runs a matrix phase -- dV^T += dO_{b-2}^T
+// P_{b-2}, dK^T += Q_{b-2}^T dS_{b-2}, S_b, dP_b, one pinned stream of
+// MFMAs -- and a VALU phase (P_b
 // from the LSE, dS_b = P_b (dP_b - D) as bf16 B operands); the two groups run
 // half an iteration apart between workgroup barriers, so one group's MFMAs
 // run beside the other's VALU work:
@@ -931,15 +933,32 @@ void bwd_dq_pp_kernel(BwdParams p) {
 #endif
 constexpr int kKvPrefetch = 4;                       // matrix-phase slots whose operands are read ahead
 
-template <int S, int NS, int NTR>
+#ifndef ATTN_BWD_DKDV_KREG
+#define ATTN_BWD_DKDV_KREG 1  // 1: each wave keeps its K rows in registers (the S products' B operands), 0: in LDS
+#endif
+
+// The lane's index within its wave, computed at the point of use: the asm
+// keeps the compiler from holding it in a register across a loop (where it
+// could be spilled and reloaded with a wait on every outstanding load).
+__device__ __forceinline__ uint32_t lane_id_here() {
+  uint32_t l = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+#endif
+  return l;
+}
+
+template <int S, int NS, int NTR, int STEPS>
 __device__ __forceinline__ void pin_kv_schedule() {
   constexpr int kMfma = 0x008, kDsRead = 0x100;
   if constexpr (S < NS) {
     // a dV / dK slot reads one transposed operand (two reads), an S / dP slot
-    // an A and a B operand (two reads)
-    if constexpr (S + kKvPrefetch < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    // an A and a B operand (two reads; one for S with K in registers)
+    constexpr int t = S + kKvPrefetch;
+    constexpr int reads = (ATTN_BWD_DKDV_KREG && t >= NTR && t < NTR + STEPS) ? 1 : 2;
+    if constexpr (t < NS) __builtin_amdgcn_sched_group_barrier(kDsRead, reads, 0);
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    pin_kv_schedule<S + 1, NS, NTR>();
+    pin_kv_schedule<S + 1, NS, NTR, STEPS>();
   }
 }
 
@@ -1048,7 +1067,7 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
                       dst + (iso ? QD_ELEMS : 0) + rr * 512);
     } else if (wv < 2) {
       const uint32_t r0 = bq < nblk ? (uint32_t)(qstart + bq * kRows) * 4u : (uint32_t)L * 4u;
-      attn::dma_dword(wv == 0 ? l_rsrc : d_rsrc, r0 + 4u * lane, dst + ROWS_OFF + wv * 128);
+      attn::dma_dword(wv == 0 ? l_rsrc : d_rsrc, r0 + 4u * lane_id_here(), dst + ROWS_OFF + wv * 128);
     }
   };
 
@@ -1064,6 +1083,7 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
   // (B is P or dS in registers), S / dP slots a row chunk of block bcur and
   // of this wave's K or V rows
   struct Ops { bf16x8_t a, b; };
+  bf16x8_t kreg[STEPS];                                           // with ATTN_BWD_DKDV_KREG, after the prologue
   auto read_op = [&] __device__ (int s, const lds_u16_t* sprev, const lds_u16_t* scur) __attribute__((always_inline))
       -> Ops {
     Ops o;
@@ -1074,7 +1094,8 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
     } else {
       const int q = s - NTR, isdp = q >= STEPS, ks = isdp ? q - STEPS : q;
       o.a = read_row_p<D>(scur + (isdp ? QD_ELEMS : 0), rq, ks, 0);
-      o.b = *(const lds_bf16x8_t*)(lds + (isdp ? KV_ELEMS : 0) + kvoff[ks]);
+      if (ATTN_BWD_DKDV_KREG && !isdp) o.b = kreg[ks];
+      else o.b = *(const lds_bf16x8_t*)(lds + (isdp ? KV_ELEMS : 0) + kvoff[ks]);
     }
     return o;
   };
@@ -1106,7 +1127,7 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
       // a request after the last MFMA of each stride of slots (measured: mid-stride −0.5 %, first slot −1.5 %)
       if (DMA && s % kDmaStride == kDmaStride - 1 && s / kDmaStride < ISS) dma(s / kDmaStride, bnext, dst);
     }
-    pin_kv_schedule<0, NS, NTR>();
+    pin_kv_schedule<0, NS, NTR, STEPS>();
   };
   // VALU phase of block bq (S, dP in sacc, pacc; LSE and D rows in its slot)
   auto valu = [&] __device__ (int bq, const lds_u16_t* sq) __attribute__((always_inline)) {
@@ -1147,12 +1168,19 @@ void bwd_dkdv_pp_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #endif
+  if (ATTN_BWD_DKDV_KREG) {
+#pragma unroll
+    for (int ks = 0; ks < STEPS; ++ks) kreg[ks] = *(const lds_bf16x8_t*)(lds + kvoff[ks]);
+  }
   using True = GroupTag<true>;
   using False = GroupTag<false>;
   auto run = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
     constexpr bool G0 = decltype(grp_tag)::value;
     int c0 = 0;                                                   // (2j) mod 5
     if (G0) prefetch(slot(3));                                    // matrix(0): block -2
+    // not peeled: a peeled first iteration gets its own register assignment,
+    // and at d = 128 the copies between the two spill registers
+#pragma clang loop unroll(disable)
     for (int j = 0; j <= niter; ++j) {
       auto m5 = [&] __device__ (int a) __attribute__((always_inline)) { return a >= 5 ? a - 5 : a; };
       const int s_even = c0, s_odd = m5(c0 + 1), s_even_m2 = m5(c0 + 3), s_odd_m2 = m5(c0 + 4);
