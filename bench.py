@@ -587,7 +587,7 @@ def main():
         st = torch.zeros(4, dtype=torch.int64, device="cuda")
         ea.fwd(q, k, v, o=o, lse=lse, cu_seqlens=cu, max_seqlen=inp["N"], causal=wl.causal,
                scale=inp["scale"], rescale_threshold_log2=args.tau, poly_exp_sixteenths=args.poly,
-               schedule=args.schedule, stats=st, stream=stream)
+               schedule=args.schedule, stats=st, block_mask=bmask_dev, stream=stream)
         torch.cuda.synchronize()
         considered, taken, tiles, items = (int(x) for x in st.cpu())
         out["stats"] = {"rescale_considered": considered, "rescale_taken": taken,
