@@ -27,15 +27,16 @@
 // two groups that alternate matrix and VALU phases as the forward kernel
 // does: the dQ kernel as one 8-wave workgroup of 256 queries whose waves each
 // do all three products; the dK/dV kernel, up to d = 128, as one 8-wave
-// workgroup of 128 keys whose two groups split the query blocks, with K and V
-// read from LDS, and at (192, 128) as one 8-wave workgroup whose two halves
-// split the products between them (earlier kernels remain as build
-// options).  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
+// workgroup of 128 keys whose two groups split the query blocks, with K in
+// registers and V read from LDS, and at (192, 128) as one 8-wave workgroup
+// whose two halves split the products between them (earlier kernels remain
+// as build options).  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
 // accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
-//   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; K, V rows from LDS
-//                                               up to d = 128, in registers at (192, 128))
+//   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; up to d = 128 K rows
+//                                               in registers and V rows from LDS, both in
+//                                               registers at (192, 128))
 //               dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by the transposing read);
 //               at (192, 128) S, P, dV^T in one wave group and dP, dS, dK^T in the other
 // With the streamed tile's rows read in an order with bits 2 and 3 of the
