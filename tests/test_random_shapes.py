@@ -16,7 +16,7 @@ from _gpu import TOL_LSE, TOL_O_MAX, TOL_O_MEAN, say, to_dev, torch_cuda
 pytestmark = pytest.mark.gpu
 
 DIMS = [(64, 64), (128, 128), (192, 128)]
-N_CASES = 12
+N_CASES = 24
 
 
 def draw_case(i):
