@@ -26,7 +26,7 @@ struct BwdParams {
   float c;                    // scale * log2(e)
 };
 
-int block_rows();             // key rows per dK/dV workgroup (the default dQ kernel takes 256 query rows each)
+int block_rows();             // key rows per dK/dV workgroup (the dQ kernel takes 256 query rows each)
 hipError_t launch_bwd(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
 
 }  // namespace attn_grad

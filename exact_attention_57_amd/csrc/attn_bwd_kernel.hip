@@ -29,9 +29,9 @@
 // do all three products; the dK/dV kernel, up to d = 128, as one 8-wave
 // workgroup of 128 keys whose two groups split the query blocks, with K in
 // registers and V read from LDS, and at (192, 128) as one 8-wave workgroup
-// whose two halves split the products between them (earlier kernels remain
-// as build options).  The matrix products are v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators:
+// whose two halves split the products between them (at d <= 128 too with
+// ATTN_BWD_DKDV_PP=0).  The matrix products are v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators:
 //   dQ kernel   S^T = K Q^T, dP^T = V dO^T     (K, V rows from LDS; Q, dO in registers)
 //               dQ^T += K^T dS^T               (K^T by the transposing LDS read)
 //   dK/dV       S = Q K^T, dP = dO V^T         (Q, dO rows from LDS; up to d = 128 K rows
@@ -84,9 +84,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 int block_rows() { return kBlock; }
 
-// LDS layouts of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
-// bytes): chunk c of row r sits at position c ^ f(r).
-//  * row layout, read 16 bytes per lane with 16 consecutive rows per
+// LDS layout of a tile of rows r with D bf16 columns (R = D/8 chunks of 16
+// bytes): chunk c of row r sits at position c ^ f(r).  The row layout is
+//    read 16 bytes per lane with 16 consecutive rows per
 //    quarter-wave, and by ds_read_b64_tr_b16 (4 rows x 4 consecutive chunks
 //    per half-wave, rows r0..r0+3 with r0 a multiple of 4): for R = 16 every
 //    row starts at bank 0, and f(r) = 4 (r mod 4) + (r/4) mod 4 (the two
@@ -95,24 +95,16 @@ int block_rows() { return kBlock; }
 //    transposing read apart; for R = 8 or 24 a row starts on alternate halves
 //    of the 64 banks, so the 4-bank group of chunk c of row r is
 //    (c ^ f(r) ^ 8 (r mod 2)) mod 16, and f(r) = 4 b1(r) + (r/4) mod 4 (bits of
-//    r/2 rotated) does the same.  Tiles read both ways are stored once;
-//  * transposed layout (only the 4-wave register-staged dQ kernel keeps a
-//    second copy in it), read by ds_read_b64_tr_b16 (4 rows x 4 chunks per
-//    half-wave): f(r) = 4 (r mod 4) (R = 16), 4 ((r/2) mod 2) (R = 8 or 24).
-// Both are invariant under a shift of r by a multiple of 16 and keep
-// c ^ f(r) < R: for R = 16 both are 4-bit values, for R = 8 and 24 f < 8
-// keeps a chunk inside its aligned group of 8.
+//    r/2 rotated) does the same.  Tiles read both ways are stored once.
+// f is invariant under a shift of r by a multiple of 16 and keeps c ^ f(r) < R:
+// for R = 16 it is a 4-bit value, for R = 8 and 24 f < 8 keeps a chunk inside
+// its aligned group of 8.
 template <int D>
 struct RowSwz {
   static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
   __device__ static int f(int r) {
     return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
-};
-template <int D>
-struct TrSwz {
-  static_assert(D == 64 || D == 128 || D == 192, "head dims 64, 128 and 192");
-  __device__ static int f(int r) { return (D == 128) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // Two fp32 values -> two bf16 (round to nearest even) in one dword, low first.
@@ -199,46 +191,16 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdParams p) {
   }
 }
 
-// ---- tiles: global -> registers (rows past L read as zeros) -> LDS.
-template <int D, int NT = kThreads>
-struct TileRegs {
-  static constexpr int N = kTile * D / 8 / NT;
-  u32x4_t c[N];
-};
-template <int D, int NT = kThreads>
-__device__ __forceinline__ void tile_load(TileRegs<D, NT>& t, const uint16_t* base, int64_t row_stride, int row0,
-                                          int L, int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D, NT>::N; ++i) {
-    const int idx = i * NT + tid, r = idx / CPR, ch = idx % CPR;
-    const int row = row0 + r;
-    t.c[i] = (row < L) ? *(const u32x4_t*)(base + (int64_t)row * row_stride + ch * 8) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
-template <int D, bool ROW, bool TR, int NT = kThreads>
-__device__ __forceinline__ void tile_store(const TileRegs<D, NT>& t, lds_u16_t* row_l, lds_u16_t* tr_l, int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D, NT>::N; ++i) {
-    const int idx = i * NT + tid, r = idx / CPR, ch = idx % CPR;
-    if (ROW) *(lds_u32x4_t*)(row_l + r * D + ((ch ^ RowSwz<D>::f(r)) * 8)) = t.c[i];
-    if (TR) *(lds_u32x4_t*)(tr_l + r * D + ((ch ^ TrSwz<D>::f(r)) * 8)) = t.c[i];
-  }
-}
-
-// Per-lane LDS element offsets.  Row reads (A operand, 32 rows in sigma order,
-// k-step s: 8 columns from 16 s + 8 g); transposed reads (A operand: columns
-// db*32 + (lane % 32) at 8 consecutive rows from 8 g, as two 4-row reads),
-// from a tile in the transposed layout, or in the row layout when TR_ROW
-// (a tile stored once for both kinds of read).
-template <int D, bool TR_ROW = false>
+// Per-lane LDS element offsets in a row-layout tile.  Row reads (A operand,
+// 32 rows in sigma order, k-step s: 8 columns from 16 s + 8 g); transposed
+// reads (A operand: columns db*32 + (lane % 32) at 8 consecutive rows from
+// 8 g, as two 4-row reads; the row layout's swizzle differs between the two
+// groups of 4 rows, so each has its own offset).
+template <int D>
 struct Reads {
   int row[D / 16];
   int tr[D / 32];
-  // rows 4..7 of a transposed read: the transposed layout's swizzle is the
-  // same 4 rows further on, the row layout's (r/2 mod 8) is not
-  int tr_hi[TR_ROW ? D / 32 : 1];
+  int tr_hi[D / 32];
   __device__ Reads(int lane) {
     const int g = lane / 32, sig = sigma(lane % 32);
 #pragma unroll
@@ -250,21 +212,20 @@ struct Reads {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int d = db * 32 + 16 * (lg % 2) + 4 * (sl % 4);
-      const int sw = TR_ROW ? RowSwz<D>::f(vrow) : TrSwz<D>::f(vrow);
-      tr[db] = vrow * D + (((d / 8) ^ sw) * 8) + (d % 8);
-      if constexpr (TR_ROW) tr_hi[db] = (vrow + 4) * D + (((d / 8) ^ RowSwz<D>::f(vrow + 4)) * 8) + (d % 8);
+      tr[db] = vrow * D + (((d / 8) ^ RowSwz<D>::f(vrow)) * 8) + (d % 8);
+      tr_hi[db] = (vrow + 4) * D + (((d / 8) ^ RowSwz<D>::f(vrow + 4)) * 8) + (d % 8);
     }
   }
 };
-template <int D, bool TR_ROW>
-__device__ __forceinline__ bf16x8_t read_row(const lds_u16_t* tile, const Reads<D, TR_ROW>& rd, int s, int blk) {
+template <int D>
+__device__ __forceinline__ bf16x8_t read_row(const lds_u16_t* tile, const Reads<D>& rd, int s, int blk) {
   return *(const lds_bf16x8_t*)(tile + rd.row[s] + blk * 32 * D);
 }
 // rows r0 .. r0+15 (r0 a multiple of 16), column block db
-template <int D, bool TR_ROW>
-__device__ __forceinline__ bf16x8_t read_tr(const lds_u16_t* tile, const Reads<D, TR_ROW>& rd, int db, int r0) {
+template <int D>
+__device__ __forceinline__ bf16x8_t read_tr(const lds_u16_t* tile, const Reads<D>& rd, int db, int r0) {
   const lds_u16_t* a = tile + rd.tr[db] + r0 * D;
-  const lds_u16_t* a_hi = TR_ROW ? tile + rd.tr_hi[db] + r0 * D : a + 4 * D;
+  const lds_u16_t* a_hi = tile + rd.tr_hi[db] + r0 * D;
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a_hi));
   const i16x4_t both[2] = {lo, hi};
@@ -311,263 +272,10 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
   }
 }
 
-// ---- dQ: one workgroup per block of 128 query rows of one (sequence, head).
-// Two waves per SIMD (two workgroups per CU) up to d_qk = 128; at d_qk = 192
-// the resident Q, dO and dQ accumulators need one wave's 512 registers.
-template <int DQK>
-constexpr int dq_waves_per_simd() { return DQK > 128 ? 1 : 2; }
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<DQK>(), dq_waves_per_simd<DQK>())))
-void bwd_dq_kernel(BwdParams p) {
-  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
-  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
-  constexpr int TILE_ELEMS = 2 * K_ELEMS + V_ELEMS;
-  constexpr int STAGE_ELEMS = kWaves * kRows * (DQK + 8);
-  constexpr int LDS_ELEMS = TILE_ELEMS > STAGE_ELEMS ? TILE_ELEMS : STAGE_ELEMS;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
-  lds_u16_t* const lds = (lds_u16_t*)smem;
-  lds_u16_t* const k_row = lds;
-  lds_u16_t* const k_tr = lds + K_ELEMS;
-  lds_u16_t* const v_row = lds + 2 * K_ELEMS;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
-  int h, b, blk;
-  decode_block(p, CAUSAL, h, b, blk);
-  int seq0, L;
-  seq_range(p, b, seq0, L);
-  const int q0 = blk * kBlock;
-  if (q0 >= L) return;
-  const int qw0 = q0 + wave * kRows;
-  const int qrow = qw0 + lq;
-  const bool row_valid = qrow < L;
-
-  bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
-  load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
-  load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
-  const int T = total_tokens(p);
-  const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
-  const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
-  // last key this lane's query sees (-1: none, the row is past the end)
-  const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
-
-  const Reads<DQK> rk(lane);
-  const Reads<DV> rv(lane);
-  const int kend = CAUSAL ? min(L, q0 + kBlock) : L;
-  const int ntiles = (kend + kTile - 1) / kTile;
-  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
-  const uint16_t* const kbase = p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK;
-  const uint16_t* const vbase = p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV;
-
-  f32x16_t dqacc[QBLK];
-#pragma unroll
-  for (int i = 0; i < QBLK; ++i) dqacc[i] = f32x16_t{};
-  const f32x16_t zero = {};
-
-  TileRegs<DQK> kr;
-  TileRegs<DV> vr;
-  for (int t = 0; t < ntiles; ++t) {
-    // no register-held prefetch of the next tile: two workgroups share a CU,
-    // and the other one computes while this one loads
-    tile_load<DQK>(kr, kbase, qk_stride, t * kTile, L, tid);
-    tile_load<DV>(vr, vbase, v_stride, t * kTile, L, tid);
-    tile_store<DQK, true, true>(kr, k_row, k_tr, tid);
-    tile_store<DV, true, false>(vr, v_row, v_row, tid);
-    block_sync();
-    const int k0 = t * kTile;
-    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(k_row, rk, ks, kb);
-      f32x16_t s = zero, dp = zero;
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], qreg[ks], s, 0, 0, 0);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
-      float ds[16];
-      {
-        // keys visible to this lane's query: up to key_lim (offsets within the block)
-        const int lim = masked ? key_lim - (k0 + kb * 32 + 8 * g) : 64;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
-          ds[r] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t dsb[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dsb[jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
-        bf16x8_t a_q[QBLK];
-#pragma unroll
-        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_tr, rk, db, kb * 32 + 16 * hh);
-#pragma unroll
-        for (int db = 0; db < QBLK; ++db)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
-      }
-    }
-    block_sync();
-  }
-  store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
-}
-
-// ---- dQ with LDS DMA tiles (d_qk = d_v <= 128): one workgroup of 8 waves
-// (two per SIMD) per block of 256 query rows, so each K/V tile fetched from
-// L2 serves twice the rows of the 4-wave kernel above.  The tiles (K and V in
-// the row layout; K is also read transposed from it) are copied HBM/L2 ->
-// LDS by buffer_load ... lds, double-buffered: at the start of tile t every
-// wave issues its share of tile t+1's requests into the other buffer (last
-// read in tile t-1, before the barrier that ended it), computes tile t, then
-// waits for its requests and meets the others at the barrier, after which
-// tile t+1 is complete.  Rows past the sequence end read as zeros (the buffer
-// range ends after key L-1).  Per-wave arithmetic as in bwd_dq_kernel.  The
-// ping-pong kernel below replaces it by default (ATTN_BWD_DQ_PP).
-#ifndef ATTN_BWD_DQ_DMA
-#define ATTN_BWD_DQ_DMA 1   // 0: the 4-wave register-staged dQ kernel at every head dim
-#endif
-#ifndef ATTN_BWD_DQ_SPLIT
-#define ATTN_BWD_DQ_SPLIT 1 // at d_qk = 192: 1 = the two-group dQ kernel, 0 = the 4-wave one
-#endif
+// dQ workgroups: 8 waves of 32 query rows each
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * kWave;
 constexpr int kDqBlock = kDqWaves * kRows;           // query rows per workgroup
-
-
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_dma_kernel(BwdParams p) {
-  static_assert(DQK == DV && DQK <= 128, "DMA dQ kernel: d_qk = d_v = 64 or 128");
-  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
-  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
-  constexpr int STAGE = K_ELEMS + V_ELEMS;            // K rows (also read transposed), V rows
-  constexpr int OUT_ELEMS = kDqWaves * kRows * (DQK + 8);
-  constexpr int LDS_ELEMS = (2 * STAGE > OUT_ELEMS) ? 2 * STAGE : OUT_ELEMS;
-  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
-  constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512;   // 1 KB requests per copy
-  constexpr int REQ = K_REQ + V_REQ;
-  static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0 && REQ % kDqWaves == 0, "request split");
-  constexpr int REQ_W = REQ / kDqWaves;                // requests per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
-  lds_u16_t* const lds = (lds_u16_t*)smem;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
-  const int nblk = (p.N + kDqBlock - 1) / kDqBlock;
-  int h, b, blk;
-  decode_block_n(p, nblk, CAUSAL, h, b, blk);
-  int seq0, L;
-  seq_range(p, b, seq0, L);
-  const int q0 = blk * kDqBlock;
-  if (q0 >= L) return;                                 // uniform over the workgroup
-  const int qw0 = q0 + wave * kRows;
-  const int qrow = qw0 + lq;
-  const bool row_valid = qrow < L;
-
-  bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
-  load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
-  load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
-  const int T = total_tokens(p);
-  const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
-  const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
-  const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
-
-  const Reads<DQK, true> rk(lane);
-  const Reads<DV> rv(lane);
-  const int kend = CAUSAL ? min(L, q0 + kDqBlock) : L;
-  const int ntiles = (kend + kTile - 1) / kTile;
-  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
-  const uint32_t k_rowbytes = (uint32_t)(qk_stride * 2), v_rowbytes = (uint32_t)(v_stride * 2);
-  const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK,
-                                               (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
-  const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV,
-                                               (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
-  auto stage = [&] __device__ (int i) __attribute__((always_inline)) { return lds + i * STAGE; };
-
-  // this wave's requests for tile t into stage buffer st: request r of the
-  // tile (r = wave * REQ_W + i) fills 1 KB block rr of its copy; lane i writes
-  // the 16 bytes at LDS position 8 i of that block, i.e. chunk `pos` of row
-  // `row`, which holds the tile's chunk pos ^ f(row) of that row
-  auto issue = [&] __device__ (int t, int st) __attribute__((always_inline)) {
-    lds_u16_t* const base = stage(st);
-#pragma unroll
-    for (int i = 0; i < REQ_W; ++i) {
-      const int r = wave * REQ_W + i;                  // uniform
-      const bool isk = r < K_REQ;
-      const int rr = isk ? r : r - K_REQ;
-      const int D = isk ? DQK : DV;
-      const int e = rr * 512 + 8 * lane;               // element of the tile (row-major, D per row)
-      const int row = e / D, pos = (e % D) / 8;
-      const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
-      const uint32_t rowbytes = isk ? k_rowbytes : v_rowbytes;
-      const uint32_t lane_off = (uint32_t)row * rowbytes + (uint32_t)(pos ^ f) * 16u;
-      const uint32_t tile_off = (uint32_t)(t * kTile) * rowbytes;
-      attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off, tile_off, base + (isk ? 0 : K_ELEMS) + rr * 512);
-    }
-  };
-
-  f32x16_t dqacc[QBLK];
-#pragma unroll
-  for (int i = 0; i < QBLK; ++i) dqacc[i] = f32x16_t{};
-  const f32x16_t zero = {};
-
-  issue(0, 0);
-  attn::dma_wait_barrier<0>();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    const lds_u16_t* const k_row = stage(t & 1);
-    const lds_u16_t* const v_row = k_row + K_ELEMS;
-    const int k0 = t * kTile;
-    const bool masked = (k0 + kTile > L) || (qw0 + kRows > L) || (CAUSAL && k0 + kTile - 1 > qw0);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8_t a_s[QK_STEPS], a_p[V_STEPS];
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) a_s[ks] = read_row<DQK>(k_row, rk, ks, kb);
-      f32x16_t s = zero, dp = zero;
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[ks], qreg[ks], s, 0, 0, 0);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
-#pragma unroll
-      for (int vs = 0; vs < V_STEPS; ++vs)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
-      float ds[16];
-      {
-        const int lim = masked ? key_lim - (k0 + kb * 32 + 8 * g) : 64;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
-          ds[r] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t dsb[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dsb[jj] = pack_bf16x2(ds[8 * hh + 2 * jj], ds[8 * hh + 2 * jj + 1]);
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, dsb);
-        bf16x8_t a_q[QBLK];
-#pragma unroll
-        for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_row, rk, db, kb * 32 + 16 * hh);
-#pragma unroll
-        for (int db = 0; db < QBLK; ++db)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, dqacc[db], 0, 0, 0);
-      }
-    }
-    attn::dma_wait_barrier<0>();                       // tile t+1 has landed; stage t & 1 is free
-  }
-  store_rows<DQK>(dqacc, p.scale, lds + wave * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
-}
 
 // ---- dQ in two ping-pong wave groups: the forward kernel's schedule applied
 // to the dQ pass.  One workgroup of 8 waves per block of 256 query rows; each
@@ -591,19 +299,13 @@ void bwd_dq_dma_kernel(BwdParams p) {
 // the same code.  The dQ slots come first in the stream: their operands
 // (K_{j-1}, resident since iteration j-2) are read at the end of the wave's
 // previous phase, before the tile DMAs of the current one have landed.
-#ifndef ATTN_BWD_DQ_PP192
-#define ATTN_BWD_DQ_PP192 1 // at d_qk = 192 too (else the two-group split kernel)
-#endif
-#ifndef ATTN_BWD_DQ_PP
-#define ATTN_BWD_DQ_PP 1    // 1: the ping-pong dQ kernel (d_qk = 192: ATTN_BWD_DQ_PP192), 0: the earlier ones
-#endif
 // matrix-phase LDS operands read this many slots ahead (fewer at d_qk = 192,
 // whose six dQ blocks leave fewer registers)
 template <int DQK>
 constexpr int pp_prefetch() { return DQK > 128 ? 2 : 4; }
 
 // Per-lane LDS offsets of the row and transposing reads of a row-layout tile,
-// as Reads<D, true>, kept only once per period: for d = 64 and 192 the
+// as Reads<D>, kept only once per period: for d = 64 and 192 the
 // swizzle values are below 8, so they act within each aligned group of 8
 // chunks and the offsets of k-step s + 4 (column block db + 2) are those of s
 // (db) plus 64 elements; d = 128 has no such period.
@@ -1293,8 +995,8 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   const bool key_valid = key < L;
 
 
-  const Reads<DQK, true> rq(lane);
-  const Reads<DV, true> ro(lane);
+  const Reads<DQK> rq(lane);
+  const Reads<DV> ro(lane);
   const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
   const int ntiles = (L - qstart + kTile - 1) / kTile;
   const int nblk = ntiles * QB;
@@ -1541,204 +1243,6 @@ void bwd_dkdv_split_kernel(BwdParams p) {
   else group_body(GroupTag<false>{});
 }
 
-// ---- dQ with the work split over two wave groups, for d_qk = 192: one wave
-// doing all three products would hold Q, dO, S, dP and six dQ blocks at once,
-// more than the 256 registers of two waves per SIMD.  One workgroup of 8 waves
-// per block of 128 query rows.  Waves 0-3 (dS group) own 32 queries each, keep
-// their Q and dO rows in registers and compute, per 32-key block, S^T = K Q^T,
-// dP^T = V dO^T and dS^T = P (dP - D), which they pass through LDS (bf16,
-// lane for lane); waves 4-7 (dQ group) own the same queries and accumulate
-// dQ^T += K^T dS^T one block later.  Per block each SIMD runs 20 + 12 MFMAs,
-// the 32 of one wave doing all three products, with the other wave's matrix
-// work beside each wave's exponentials.  One barrier per block:
-//   dS group: ... | S, dP, dS(n) -> LDS | S, dP, dS(n+1) -> LDS | ...
-//   dQ group: ... | dQ(n-1)             | dQ(n)                 | ...
-// K tiles (64 keys, stored once in the row layout: the row and the
-// transposing reads are both conflict-free there) and V tiles come by LDS DMA
-// from the dQ group's waves into three buffers.  Tile u+3 is issued in
-// interval 2u+3, once block 2u+1's dQ products (interval 2u+2) have released
-// tile u's buffer, and awaited before interval 2u+5 ends: its first reader
-// runs in interval 2u+6.
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_split_kernel(BwdParams p) {
-  constexpr int QK_STEPS = DQK / 16, V_STEPS = DV / 16, QBLK = DQK / 32, KB = kTile / 32;
-  constexpr int K_ELEMS = kTile * DQK, V_ELEMS = kTile * DV;
-  constexpr int TILE_ELEMS = K_ELEMS + V_ELEMS;                        // K rows, V rows
-  constexpr int NBUF = 3;
-  constexpr int DS_ELEMS = kWaves * kWave * 16;                        // 32 x 32 bf16 per dS wave
-  constexpr int DS_HALF = DS_ELEMS / 2 / 8;                            // in 16-byte units
-  constexpr int WORK_ELEMS = NBUF * TILE_ELEMS + 2 * DS_ELEMS;
-  constexpr int STAGE_ELEMS = kWaves * kRows * (DQK + 8);
-  constexpr int LDS_ELEMS = WORK_ELEMS > STAGE_ELEMS ? WORK_ELEMS : STAGE_ELEMS;
-  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS budget");
-  constexpr int K_REQ = K_ELEMS / 512, V_REQ = V_ELEMS / 512, REQ = K_REQ + V_REQ;   // 1 KB requests
-  static_assert(K_ELEMS % 512 == 0 && V_ELEMS % 512 == 0 && REQ % kWaves == 0, "request split");
-  constexpr int REQ_W = REQ / kWaves;                                  // per dQ-group wave and tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_ELEMS];
-  lds_u16_t* const lds = (lds_u16_t*)smem;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const bool qgrp = wave >= kWaves;          // dQ group
-  const int wv = wave % kWaves;              // query slice of the wave within its group
-  const int lane = tid % kWave, g = lane / 32, lq = lane % 32;
-  int h, b, blk;
-  decode_block(p, CAUSAL, h, b, blk);
-  int seq0, L;
-  seq_range(p, b, seq0, L);
-  const int q0 = blk * kBlock;
-  if (q0 >= L) return;                       // uniform over the workgroup
-  const int qw0 = q0 + wv * kRows;
-  const int qrow = qw0 + lq;
-  const bool row_valid = qrow < L;
-  const int kend = CAUSAL ? min(L, q0 + kBlock) : L;
-  const int ntiles = (kend + kTile - 1) / kTile;
-  const int nblk = ntiles * KB;
-  const int64_t qk_stride = (int64_t)p.H * DQK, v_stride = (int64_t)p.H * DV;
-  const Reads<DQK, true> rk(lane);           // K rows and K^T, both from the row layout
-
-  auto buf = [&] __device__ (int t) __attribute__((always_inline)) { return lds + (t % NBUF) * TILE_ELEMS; };
-  // this lane's 32 bytes of wave wv's dS block, buffer i, as two 16-byte
-  // halves DS_HALF apart (each half of all lanes contiguous: conflict-free)
-  auto dslot = [&] __device__ (int i) __attribute__((always_inline)) {
-    return (lds_u32x4_t*)(lds + NBUF * TILE_ELEMS + i * DS_ELEMS + (wv * kWave + lane) * 8);
-  };
-
-  auto group_body = [&] __device__ (auto grp_tag) __attribute__((always_inline)) {
-    constexpr bool QG = decltype(grp_tag)::value;
-    if constexpr (!QG) {
-      bf16x8_t qreg[QK_STEPS], doreg[V_STEPS];
-      load_b_operand<DQK>(qreg, p.q, seq0 + qrow, p.H, h, g, row_valid);
-      load_b_operand<DV>(doreg, p.dout, seq0 + qrow, p.H, h, g, row_valid);
-      const int T = total_tokens(p);
-      const float lse2 = row_valid ? p.lse[(int64_t)h * T + seq0 + qrow] * kLog2e : 0.0f;
-      const float dq_row = row_valid ? p.delta[(int64_t)h * T + seq0 + qrow] : 0.0f;
-      // last key this lane's query sees (-1: none, the row is past the end)
-      const int key_lim = row_valid ? (CAUSAL ? min(L - 1, qrow) : L - 1) : -1;
-      const Reads<DV> rv(lane);
-      const f32x16_t zero = {};
-      block_sync();                          // the first tiles have landed
-      for (int m = 0; m < nblk; ++m) {
-        const int kb = m % KB;
-        const lds_u16_t* const k_row = buf(m / KB);
-        const lds_u16_t* const v_row = k_row + K_ELEMS;
-        // operands read in groups of at most 6 k-steps beside the resident Q and dO
-        constexpr int CH = QK_STEPS > 8 ? QK_STEPS / 2 : QK_STEPS;
-        f32x16_t s = zero, dp = zero;
-#pragma unroll
-        for (int k0 = 0; k0 < QK_STEPS; k0 += CH) {
-          bf16x8_t a_s[CH];
-#pragma unroll
-          for (int i = 0; i < CH; ++i) a_s[i] = read_row<DQK>(k_row, rk, k0 + i, kb);
-#pragma unroll
-          for (int i = 0; i < CH; ++i) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_s[i], qreg[k0 + i], s, 0, 0, 0);
-        }
-        bf16x8_t a_p[V_STEPS];
-#pragma unroll
-        for (int vs = 0; vs < V_STEPS; ++vs) a_p[vs] = read_row<DV>(v_row, rv, vs, kb);
-#pragma unroll
-        for (int vs = 0; vs < V_STEPS; ++vs)
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_p[vs], doreg[vs], dp, 0, 0, 0);
-        const int kb0 = m * 32;                // first key of the block
-        const bool masked = (kb0 + 32 > L) || (qw0 + kRows > L) || (CAUSAL && kb0 + 31 > qw0);
-        // keys visible to this lane's query: up to key_lim (offsets within the block)
-        const int lim = masked ? key_lim - (kb0 + 8 * g) : 64;
-        uint32_t dsb[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float d2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * i + e;
-            const float x = (16 * (r / 8) + (r % 8) <= lim) ? __builtin_fmaf(s[r], p.c, -lse2) : -__builtin_inff();
-            d2[e] = __builtin_amdgcn_exp2f(x) * (dp[r] - dq_row);
-          }
-          dsb[i] = pack_bf16x2(d2[0], d2[1]);
-        }
-        lds_u32x4_t* const slot = dslot(m & 1);
-        slot[0] = u32x4_t{dsb[0], dsb[1], dsb[2], dsb[3]};
-        slot[DS_HALF] = u32x4_t{dsb[4], dsb[5], dsb[6], dsb[7]};
-        block_sync();
-      }
-      block_sync();                          // the dQ group's last block
-    } else {
-      const uint32_t k_rowbytes = (uint32_t)(qk_stride * 2), v_rowbytes = (uint32_t)(v_stride * 2);
-      const attn::u32x4_t k_rsrc = attn::make_rsrc(p.k + (int64_t)seq0 * qk_stride + (int64_t)h * DQK,
-                                                   (uint32_t)((L - 1) * qk_stride * 2 + DQK * 2));
-      const attn::u32x4_t v_rsrc = attn::make_rsrc(p.v + (int64_t)seq0 * v_stride + (int64_t)h * DV,
-                                                   (uint32_t)((L - 1) * v_stride * 2 + DV * 2));
-      // this wave's requests for a tile: request r = wv * REQ_W + i fills 1 KB
-      // block rr of the K or V copy; lane i writes the 16 bytes at LDS position
-      // 8 i of that block, i.e. chunk `pos` of row `row`, which holds the
-      // tile's chunk pos ^ f(row) of that row.  Rows past the sequence end read
-      // as zeros (the buffer range ends after key L-1).  The lane offsets are
-      // the same for every tile and are computed once (the row length differs
-      // between K and V, so each costs an integer division).
-      uint32_t lane_off[REQ_W];
-#pragma unroll
-      for (int i = 0; i < REQ_W; ++i) {
-        const int r = wv * REQ_W + i;                            // uniform
-        const bool isk = r < K_REQ;
-        const int rr = isk ? r : r - K_REQ;
-        const int D = isk ? DQK : DV;
-        const int e = rr * 512 + 8 * lane;
-        const int row = e / D, pos = (e % D) / 8;
-        const int f = isk ? RowSwz<DQK>::f(row) : RowSwz<DV>::f(row);
-        lane_off[i] = (uint32_t)row * (isk ? k_rowbytes : v_rowbytes) + (uint32_t)(pos ^ f) * 16u;
-      }
-      auto issue = [&] __device__ (int t) __attribute__((always_inline)) {
-        lds_u16_t* const base = buf(t);
-#pragma unroll
-        for (int i = 0; i < REQ_W; ++i) {
-          const int r = wv * REQ_W + i;                          // uniform
-          const bool isk = r < K_REQ;
-          const int rr = isk ? r : r - K_REQ;
-          const uint32_t rowbytes = isk ? k_rowbytes : v_rowbytes;
-          attn::dma_chunk(isk ? k_rsrc : v_rsrc, lane_off[i], (uint32_t)(t * kTile) * rowbytes,
-                          base + (isk ? 0 : K_ELEMS) + rr * 512);
-        }
-      };
-      f32x16_t acc[QBLK];
-#pragma unroll
-      for (int i = 0; i < QBLK; ++i) acc[i] = f32x16_t{};
-      for (int t = 0; t < NBUF && t < ntiles; ++t) issue(t);
-      attn::dma_wait_all();
-      block_sync();
-      for (int m = 0; m <= nblk; ++m) {
-        const bool refill = (m & 1) && m >= 3 && (m + 3) / 2 < ntiles;
-        if (refill) issue((m + 3) / 2);
-        if (m >= 1) {
-          const int n = m - 1, kb = n % KB;
-          const lds_u16_t* const k_row = buf(n / KB);
-          const lds_u32x4_t* const slot = dslot(n & 1);
-          const u32x4_t praw[2] = {slot[0], slot[DS_HALF]};
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, praw[hh]);
-            bf16x8_t a_q[QBLK];
-#pragma unroll
-            for (int db = 0; db < QBLK; ++db) a_q[db] = read_tr<DQK>(k_row, rk, db, kb * 32 + 16 * hh);
-#pragma unroll
-            for (int db = 0; db < QBLK; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q[db], bop, acc[db], 0, 0, 0);
-          }
-        }
-        // the tile issued two odd intervals ago has landed before the barrier
-        // ahead of its first reader; this interval's may stay in flight
-        if (m & 1) {
-          if (refill) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(REQ_W) : "memory");
-          else attn::dma_wait_all();
-        }
-        block_sync();
-      }
-      attn::dma_wait_all();
-      store_rows<DQK>(acc, p.scale, lds + wv * kRows * (DQK + 8), p.dq, (int64_t)seq0 + qw0, L - qw0, p.H, h, lane);
-    }
-  };
-  if (qgrp) group_body(GroupTag<true>{});
-  else group_body(GroupTag<false>{});
-}
-
 template <int DQK, int DV>
 hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.N * p.H;   // at least T*H; the kernel stops at T*H
@@ -1752,23 +1256,9 @@ hipError_t launch_dims(const BwdParams& p, bool causal, hipStream_t s) {
     if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
     else hipLaunchKernelGGL((bwd_dkdv_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
   }
-  if constexpr (ATTN_BWD_DQ_PP && (DQK <= 128 || ATTN_BWD_DQ_PP192)) {
-    const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
-    if (causal) hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
-  } else if constexpr (ATTN_BWD_DQ_DMA && DQK == DV && DQK <= 128) {
-    const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
-    if (causal) hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_dma_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
-  } else {
-    if constexpr (ATTN_BWD_DQ_SPLIT && DQK > 128) {
-      if (causal) hipLaunchKernelGGL((bwd_dq_split_kernel<DQK, DV, true>), grid, dim3(kThreads2), 0, s, p);
-      else hipLaunchKernelGGL((bwd_dq_split_kernel<DQK, DV, false>), grid, dim3(kThreads2), 0, s, p);
-    } else {
-      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, p);
-    }
-  }
+  const dim3 grid8((unsigned)(p.B * p.H * ((p.N + kDqBlock - 1) / kDqBlock)));
+  if (causal) hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, true>), grid8, dim3(kDqThreads), 0, s, p);
+  else hipLaunchKernelGGL((bwd_dq_pp_kernel<DQK, DV, false>), grid8, dim3(kDqThreads), 0, s, p);
   return hipGetLastError();
 }
 
