@@ -492,6 +492,8 @@ def main():
     if args.fp8:
         if args.bwd or args.block_density is not None:
             raise SystemExit("--fp8 times the dense forward pass only")
+        if args.stats:
+            raise SystemExit("--stats reads the bf16 forward kernel's counters; the FP8 entry point has none")
         f8 = workloads.make_fp8_inputs(inp)
         q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q8", "k8", "v8"))
 
