@@ -368,6 +368,8 @@ def main():
                     help="only run a plain elementwise copy kernel (negation) over MIB MiB 5 times "
                          "(for scaling FETCH_SIZE/WRITE_SIZE counters) and print the byte counts")
     args = ap.parse_args()
+    if args.stats and (args.bwd or args.fp8):
+        raise SystemExit("--stats reads the bf16 forward kernel's counters; the backward and FP8 entry points have none")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -492,8 +494,6 @@ def main():
     if args.fp8:
         if args.bwd or args.block_density is not None:
             raise SystemExit("--fp8 times the dense forward pass only")
-        if args.stats:
-            raise SystemExit("--stats reads the bf16 forward kernel's counters; the FP8 entry point has none")
         f8 = workloads.make_fp8_inputs(inp)
         q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q8", "k8", "v8"))
 

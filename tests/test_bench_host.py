@@ -91,6 +91,17 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "single-GPU" in r.stderr
 
 
+@pytest.mark.parametrize("flag", ["--bwd", "--fp8"])
+def test_stats_only_for_the_bf16_forward(flag):
+    """--stats reads the bf16 forward kernel's counters: with the backward or
+    FP8 pass it is refused before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--stats", flag],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "--stats" in r.stderr
+
+
 def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     for rel in sum(bench.KERNEL_SOURCES.values(), []):
