@@ -90,6 +90,17 @@ def test_sequences_ending_on_tile_and_block_boundaries(dims, causal):
     full_check(inp, causal, 1.0 / np.sqrt(dims[0]), f"boundary-length sequences d{dims}", packed=True)
 
 
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_work_items_not_a_multiple_of_eight(dims, causal):
+    """37 heads over three sequences, the longest 1100 tokens: grids of
+    37 x 3 x 9 = 999 dK/dV blocks of 128 keys and 37 x 3 x 5 = 555 dQ blocks
+    of 256 queries, neither a multiple of the 8 XCDs the work order deals
+    them to; every gradient element is checked."""
+    inp = workloads.make_custom_inputs([1100, 97, 300], 37, dims[0], dims[1], seed=31)
+    full_check(inp, causal, 1.0 / np.sqrt(dims[0]), f"37 heads d{dims}", packed=True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fixed_length_ragged_tail(causal):
     inp = workloads.make_custom_inputs([300, 300], 2, 128, 128, seed=5)

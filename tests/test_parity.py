@@ -42,6 +42,20 @@ def test_ragged_packed_all_elements(dims, causal):
     full_check(inp, f"ragged {dims} causal={causal}")
 
 
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_work_items_not_a_multiple_of_eight(dims, causal):
+    """37 heads over three sequences, the longest 1100 tokens: a grid of
+    37 x 3 x 5 = 555 work items of 256 rows (the grid follows the longest
+    sequence), not a multiple of the 8 XCDs the default order deals them to,
+    with several (sequence, head) pairs per XCD; every item must run once."""
+    inp = workloads.make_custom_inputs([1100, 97, 300], H=37, d_qk=dims[0], d_v=dims[1], seed=31)
+    inp["causal"] = causal
+    inp["scale"] = 1.0 / np.sqrt(dims[0])
+    say(f"case: 37 heads dims={dims} causal={causal}")
+    full_check(inp, f"37 heads {dims} causal={causal}", packed=True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fixed_length_ragged_tail(causal):
     inp = workloads.make_custom_inputs([333, 333], H=2, d_qk=128, d_v=128, seed=12)
