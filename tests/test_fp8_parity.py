@@ -165,6 +165,19 @@ def test_fp8_ragged_packed_all_elements(causal, dims):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_fp8_many_heads_work_items_not_a_multiple_of_eight(causal):
+    """37 heads over three sequences, the longest 1100 tokens: a grid of
+    37 x 3 x 5 = 555 work items, not a multiple of the 8 XCDs the work order
+    deals them to; every element within the derived bound."""
+    inp = workloads.make_custom_inputs([1100, 97, 300], H=37, d_qk=128, d_v=128, seed=31)
+    inp["causal"] = causal
+    f = fp8_inputs(inp, prescale=(4.0, 2.0, 8.0))
+    say(f"case: fp8 37 heads causal={causal}")
+    o, lse = run_fp8(f)
+    check(f, o, lse, f"37 heads causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp8_fixed_length_ragged_tail(causal):
     inp = workloads.make_custom_inputs([333, 333], H=2, d_qk=128, d_v=128, seed=12)
     inp["causal"] = causal
